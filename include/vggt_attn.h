@@ -1,0 +1,149 @@
+/*
+ * vggt_attn.h -- C ABI of an MI355X (gfx950) library for the forward pass of VGGT's global
+ * cross-frame self-attention, out = softmax(Q K^T / sqrt(d)) V, over N frames of
+ * L = n_special + gh*gw tokens, in four forms:
+ *
+ *   dense        every token is a key ("AVGGT: Rethinking Global Attention for Accelerating
+ *                VGGT", papernotes.org CVPR 2026 notes, 关键设计 2, the attention equation);
+ *   SGA          all queries kept; K/V restricted to the set S = the first patch of every
+ *                s_h x s_w window, every camera/register token, and (VGGT) all of frame 0;
+ *                sigma = s_h*s_w with 2->(1,2), 4->(2,2), 6->(2,3), 9->(3,3) (same notes,
+ *                关键设计 2; gist.science summary of the paper, "Technische Zusammenfassung" 2.B);
+ *   enhanced SGA S plus a diagonal self term and one mean K/V per compressed frame, all under a
+ *                single softmax (AVGGT notes, 关键设计 3); the weight of the mean term is a flag:
+ *                unit, or ln|D_f| added to its logit, the size bias of "RegimeVGGT: Layer-Wise
+ *                Spatially Preserving Redundancy Removal ..." (papernotes.org NeurIPS 2026
+ *                notes, 关键设计 2);
+ *   G2F          Global-to-Frame: each frame attends only to its own L tokens (AVGGT notes,
+ *                关键设计 1).
+ *
+ * Conventions shared by every entry point
+ *   - Tensors q, k, v, out are dense row-major [H][T][d], T = N*L, batch 1.  Within a frame
+ *     the n_special camera/register tokens come first, then the patches row-major (token
+ *     f*L + n_special + r*gw + c is patch (r, c) of frame f).
+ *   - Device pointers are HIP device addresses owned by the caller; the library never
+ *     allocates, frees or retains device memory.  `workspace` is caller-owned scratch of at
+ *     least vggt_attn_workspace_bytes() bytes; its contents between calls are not meaningful
+ *     except as documented for vggt_attn_pack / vggt_attn_copy_index_set.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).  Device work is
+ *     only enqueued; execution errors surface at the caller's next synchronisation.
+ *   - Every int-returning call returns a vggt_attn_status (0 = success).  On failure nothing is
+ *     enqueued and vggt_attn_last_error() holds a description (thread-local).
+ *   - Plans are immutable host objects: concurrent calls with one plan are safe as long as
+ *     each call has its own workspace and output.
+ */
+#ifndef VGGT_ATTN_H
+#define VGGT_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  VGGT_ATTN_OK = 0,
+  VGGT_ATTN_EINVAL = -1,       /* invalid argument or descriptor                          */
+  VGGT_ATTN_EUNSUPPORTED = -2, /* valid request this build does not implement (head_dim) */
+  VGGT_ATTN_ENOSPC = -3,       /* workspace smaller than vggt_attn_workspace_bytes()      */
+  VGGT_ATTN_EALIGN = -4,       /* a device pointer is not 16-byte aligned                 */
+  VGGT_ATTN_EALIAS = -5,       /* out overlaps q, k, v or the workspace                   */
+  VGGT_ATTN_EHIP = -6          /* a HIP runtime call or kernel launch failed              */
+} vggt_attn_status;
+
+/* Element types. */
+enum { VGGT_ATTN_BF16 = 0, VGGT_ATTN_FP32 = 1 };
+
+/* Form flags (bitwise OR). */
+enum {
+  VGGT_ATTN_G2F = 1u << 0,        /* per-frame attention; needs sigma == 1, no DIAG/MEAN       */
+  VGGT_ATTN_REF_DENSE = 1u << 1,  /* frame 0 kept dense as K/V (VGGT); clear = every frame
+                                     compressed alike (pi^3) -- AVGGT notes, 关键设计 2         */
+  VGGT_ATTN_DIAG = 1u << 2,       /* diagonal self term for queries whose token is not in S    */
+  VGGT_ATTN_MEAN = 1u << 3,       /* one mean K/V per compressed frame, over its dropped patches */
+  VGGT_ATTN_MEAN_COUNT = 1u << 4  /* mean logit += ln|D_f|, else the mean is one plain token    */
+};
+
+typedef struct vggt_attn_plan_s vggt_attn_plan_t;
+
+/* Where each part of a workspace lives, in bytes from its start (all 256-byte aligned), and
+ * the packed key geometry.  Packed keys of one head form `segments` segments of
+ * `segment_rows` rows (one segment per head in the global forms, one per frame under G2F);
+ * rows [0, keys_per_segment) are valid, the rest are zero padding up to a multiple of 64. */
+typedef struct {
+  int64_t segments;          /* per head                                                     */
+  int64_t segment_rows;      /* padded rows per segment (multiple of 64)                     */
+  int64_t keys_per_segment;  /* |S| + M (global forms) or L (G2F)                            */
+  int64_t off_index;         /* int32[|S|]: S as ascending global token ids                  */
+  int64_t off_dcount;        /* int32[N]: |D_f| per frame (0 for dense frames)               */
+  int64_t off_means;         /* [H][M][2][d] input dtype: mean key, mean value               */
+  int64_t off_kpack;         /* [H][segments*segment_rows][d] input dtype                    */
+  int64_t off_vpack;         /* bf16: [H][rows/64][d][64] key-minor tiles (see below);
+                                fp32: [H][rows][d]                                           */
+  int64_t total_bytes;
+} vggt_attn_layout_t;
+
+/* Build a plan (host only; no device call is made, so it works without a GPU).
+ * Operation: AVGGT notes 关键设计 1-3 as summarised at the top of this header.
+ *   frames >= 1, grid_h >= 1, grid_w >= 1, 0 <= n_special, heads >= 1;
+ *   head_dim must be 64 (else EUNSUPPORTED);
+ *   sigma in {1, 2, 4, 6, 9} (else EINVAL); sigma = 1 is dense attention (DIAG/MEAN then have
+ *     no effect: no token is dropped);
+ *   G2F requires sigma == 1 and neither DIAG nor MEAN (EINVAL);
+ *   (in_dtype, out_dtype) in {(BF16, FP32), (BF16, BF16), (FP32, FP32)} (EINVAL);
+ *   T = frames*L must not exceed 8,000,000 and heads 4096 (EINVAL).
+ * On success *out owns a plan to be released with vggt_attn_plan_destroy(). */
+int vggt_attn_plan(vggt_attn_plan_t** out, int frames, int grid_h, int grid_w, int n_special,
+                   int heads, int head_dim, int sigma, unsigned flags, int in_dtype,
+                   int out_dtype);
+
+/* Release a plan (NULL is ignored). */
+void vggt_attn_plan_destroy(vggt_attn_plan_t* plan);
+
+/* Workspace size in bytes for vggt_attn_forward / vggt_attn_pack (0 if plan is NULL). */
+size_t vggt_attn_workspace_bytes(const vggt_attn_plan_t* plan);
+
+/* Sizes of the call: n_kv = |S| (L under G2F), n_mean = M (number of mean keys), n_diag =
+ * number of queries with a diagonal term, flops = algorithmic FLOPs of one forward:
+ * 4*d*H*(T*(|S|+M) + n_diag) for the global forms, 4*d*H*N*L^2 for G2F (QK^T and PV
+ * multiply-adds of attended keys only).  Any output pointer may be NULL. */
+int vggt_attn_counts(const vggt_attn_plan_t* plan, int64_t* n_kv, int64_t* n_mean,
+                     int64_t* n_diag, double* flops);
+
+/* Workspace layout of the plan (see vggt_attn_layout_t). */
+int vggt_attn_layout(const vggt_attn_plan_t* plan, vggt_attn_layout_t* out);
+
+/* Full forward: vggt_attn_pack followed by vggt_attn_attend on `stream`.
+ * q, k, v: [H][T][d] of the input dtype; out: [H][T][d] of the output dtype; every pointer
+ * 16-byte aligned; out must not overlap q, k, v or the workspace (EALIAS). */
+int vggt_attn_forward(const vggt_attn_plan_t* plan, const void* q, const void* k, const void* v,
+                      void* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Gather/pack stage (AVGGT notes 关键设计 2 and 3): writes S (ascending token ids) and |D_f|
+ * into the workspace, the per-frame mean key/value of the dropped patches (float32 sums
+ * divided by |D_f|, rounded to the input dtype), and the packed keys and values: rows
+ * [0,|S|) are exact copies of K/V rows of S, rows [|S|, |S|+M) the means, padding rows zero.
+ * Under G2F (and sigma = 1) it packs every token, frame by frame.  Reads k and v only. */
+int vggt_attn_pack(const vggt_attn_plan_t* plan, const void* k, const void* v, void* workspace,
+                   size_t workspace_bytes, void* stream);
+
+/* Attention stage on a workspace already filled by vggt_attn_pack for the same plan and the
+ * same k, v (k and v are read again for the diagonal term).  Writes every element of out. */
+int vggt_attn_attend(const vggt_attn_plan_t* plan, const void* q, const void* k, const void* v,
+                     void* out, const void* workspace, size_t workspace_bytes, void* stream);
+
+/* Copy S (|S| int32, ascending token ids) and |D_f| (N int32) from a packed workspace to host
+ * memory; waits for `stream`.  Either host pointer may be NULL.  Under G2F there is no S and
+ * host_idx is left untouched. */
+int vggt_attn_copy_index_set(const vggt_attn_plan_t* plan, const void* workspace,
+                             int32_t* host_idx, int32_t* host_dcount, void* stream);
+
+/* Thread-local description of the last failure on this thread ("" if none). */
+const char* vggt_attn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VGGT_ATTN_H */

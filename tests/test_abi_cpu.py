@@ -1,0 +1,121 @@
+"""CPU-side checks of the C ABI: the library loads, exports every function the header declares,
+and its host plan agrees with the oracle's counts (no device call is made)."""
+import os
+import re
+
+import pytest
+
+import oracle
+from oracle import Desc
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def ensure_built():
+    import vggt_global_attention_attn_amd as va
+    if not os.path.exists(va.LIB_PATH):
+        from vggt_global_attention_attn_amd.build import build
+        build()
+    return va
+
+
+@pytest.fixture(scope="module")
+def va():
+    return ensure_built()
+
+
+def declared_functions():
+    names = set()
+    inc = os.path.join(ROOT, "include")
+    for fn in os.listdir(inc):
+        if fn.endswith(".h"):
+            text = open(os.path.join(inc, fn)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names.update(re.findall(r"\b(vggt_attn_[a-z_]+)\s*\(", text))
+    return names
+
+
+def test_library_exports_every_declared_symbol(va):
+    names = declared_functions()
+    assert {"vggt_attn_plan", "vggt_attn_forward"} <= names
+    lib = va.lib()
+    for n in sorted(names):
+        assert hasattr(lib, n), f"{n} not exported"
+    assert set(va.EXPORTS) == names
+
+
+CONFIGS = [
+    Desc(4, 8, 8, 2, sigma=4, diag=True, mean=True),
+    Desc(4, 8, 8, 2, sigma=4, diag=True, mean=True, ref_dense=False),
+    Desc(32, 37, 37, 16, sigma=1),
+    Desc(100, 37, 37, 16, sigma=4, diag=True, mean=True),
+    Desc(200, 37, 37, 16, g2f=True),
+    Desc(200, 37, 37, 16, sigma=9, diag=True, mean=True),
+    Desc(800, 37, 37, 16, sigma=6, diag=True, mean=True),
+    Desc(3, 5, 7, 2, sigma=2, mean=True, mean_count=True),
+    Desc(3, 1, 1, 2, sigma=9, diag=True, mean=True),  # every window is a single patch: nothing dropped
+    Desc(2, 2, 1, 1, sigma=2, diag=True, mean=True),  # one column: (1,2) windows keep everything
+]
+
+
+@pytest.mark.parametrize("desc", CONFIGS, ids=lambda d: f"{d.frames}x{d.grid_h}x{d.grid_w}-s{d.sigma}-g2f{int(d.g2f)}")
+def test_plan_counts_match_oracle(va, desc):
+    p = va.Plan(desc.frames, desc.grid_h, desc.grid_w, desc.heads, sigma=desc.sigma, ref_dense=desc.ref_dense,
+                diag=desc.diag, mean=desc.mean, mean_count=desc.mean_count, g2f=desc.g2f)
+    c = p.counts()
+    o = oracle.counts(desc)
+    assert (c["n_kv"], c["n_mean"], c["n_diag"]) == (o["n_kv"], o["n_mean"], o["n_diag"])
+    d4H = 4 * desc.head_dim * desc.heads
+    if desc.g2f:
+        flops = d4H * desc.frames * desc.L ** 2
+    else:
+        flops = d4H * (desc.T * (o["n_kv"] + o["n_mean"]) + o["n_diag"])
+    assert c["flops"] == pytest.approx(flops, rel=1e-12)
+    lay = p.layout()
+    assert lay["segment_rows"] % 64 == 0 and lay["segment_rows"] >= lay["keys_per_segment"]
+    for key in ("off_index", "off_dcount", "off_means", "off_kpack", "off_vpack", "total_bytes"):
+        assert lay[key] % 256 == 0
+    assert lay["total_bytes"] == p.workspace_bytes
+
+
+def test_config5_sizes(va):
+    p = va.Plan(800, 37, 37, 16, sigma=6, diag=True, mean=True)
+    c = p.counts()
+    assert c["n_kv"] == 202722 and c["n_mean"] == 799 and c["n_diag"] == 896478
+    assert c["flops"] == pytest.approx(916.32e12, rel=1e-4)
+    lay = p.layout()
+    assert lay["segment_rows"] == 203584 and lay["keys_per_segment"] == 203521
+
+
+@pytest.mark.parametrize("kwargs,code", [
+    (dict(sigma=3), "EINVAL"),
+    (dict(sigma=0), "EINVAL"),
+    (dict(head_dim=128), "EUNSUPPORTED"),
+    (dict(g2f=True, sigma=4), "EINVAL"),
+    (dict(g2f=True, mean=True), "EINVAL"),
+    (dict(in_dtype="fp32", out_dtype="bf16"), "EINVAL"),
+    (dict(flags=1 << 7), "EINVAL"),
+    (dict(frames=0), "EINVAL"),
+    (dict(heads=0), "EINVAL"),
+    (dict(frames=6000, grid_h=37, grid_w=37), "EINVAL"),  # 8.2M tokens > limit
+])
+def test_plan_rejects(va, kwargs, code):
+    base = dict(frames=4, grid_h=8, grid_w=8, heads=2)
+    base.update(kwargs)
+    with pytest.raises(va.VggtAttnError) as ei:
+        va.Plan(**base)
+    assert ei.value.status == code
+    assert va.lib().vggt_attn_last_error()
+
+
+def test_null_arguments(va):
+    import ctypes
+    L = va.lib()
+    assert L.vggt_attn_plan(None, 1, 1, 1, 5, 1, 64, 1, 0, 0, 0) == -1
+    assert L.vggt_attn_workspace_bytes(None) == 0
+    assert L.vggt_attn_counts(None, None, None, None, None) == -1
+    p = va.Plan(4, 8, 8, 2)
+    assert L.vggt_attn_forward(p.handle, None, None, None, None, None, 0, None) == -1
+    assert L.vggt_attn_pack(p.handle, None, None, None, 0, None) == -1
+    L.vggt_attn_plan_destroy(None)
+    assert L.vggt_attn_counts(p.handle, None, None, None, None) == 0

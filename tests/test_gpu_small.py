@@ -1,0 +1,203 @@
+"""GPU parity at sizes the oracle finishes in seconds: several key and query tiles, ragged
+tails, every form (dense, SGA sigma 2/4/6/9, enhanced SGA with UNIT and COUNT means, pi^3
+without a dense frame, G2F), both output types, plus the bit-exact index set and packed rows,
+V = 1, determinism, a NaN-poisoned workspace and the C ABI's error codes.  Every call goes
+through the C ABI of libvggt_attn.so."""
+import ctypes
+import zlib
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import Desc
+from tests.gpu_util import assert_close, errors, inputs_for, plan_kwargs, to_device
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    # frames, gh, gw, heads, flags                               (label)
+    (Desc(3, 5, 7, 2, sigma=1), "dense-tiny-ragged"),
+    (Desc(3, 5, 7, 2, sigma=6, diag=True, mean=True), "sga6-enh-tiny"),
+    (Desc(6, 13, 11, 2, sigma=2), "sga2-plain"),
+    (Desc(6, 13, 11, 2, sigma=4, diag=True, mean=True), "sga4-enh"),
+    (Desc(6, 13, 11, 2, sigma=6, diag=True, mean=True, mean_count=True), "sga6-enh-count"),
+    (Desc(6, 13, 11, 2, sigma=9, diag=True, mean=True, ref_dense=False), "sga9-enh-pi3"),
+    (Desc(5, 13, 11, 3, g2f=True), "g2f-small"),
+    (Desc(7, 37, 37, 2, sigma=4, diag=True, mean=True), "sga4-enh-37x37"),
+    (Desc(3, 37, 37, 2, sigma=1), "dense-37x37"),
+    (Desc(4, 37, 37, 2, g2f=True), "g2f-37x37"),
+    (Desc(9, 37, 37, 1, sigma=9, diag=True, mean=True, mean_count=True), "sga9-enh-count-37x37"),
+]
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import vggt_global_attention_attn_amd as va
+    return va
+
+
+def run(va, desc, q, k, v, out_dtype="fp32", in_dtype="bf16"):
+    import torch
+    plan = va.Plan(**plan_kwargs(desc, in_dtype, out_dtype))
+    qd, kd, vd = to_device(q), to_device(k), to_device(v)
+    out = plan.new_output()
+    ws = plan.new_workspace()
+    plan.forward(qd, kd, vd, out, ws)
+    torch.cuda.synchronize()
+    return plan, out.float().cpu().numpy(), ws, (qd, kd, vd)
+
+
+@pytest.mark.parametrize("desc,label", CASES, ids=[c[1] for c in CASES])
+def test_parity_bf16(lib, desc, label):
+    print(f"[parity] {label} {desc}", flush=True)
+    q, k, v = inputs_for(desc, "bf16", seed=zlib.crc32(label.encode()) % 1000)
+    _, got, _, _ = run(lib, desc, q, k, v)
+    ref = oracle.attention(q, k, v, desc, workers=4)
+    print(label, "max-abs %.3e rel-L2 %.3e" % errors(got, ref))
+    assert_close(got, ref, fp32=False, label=label)
+
+
+@pytest.mark.parametrize("desc,label", CASES[:6], ids=[c[1] for c in CASES[:6]])
+def test_parity_bf16_out(lib, desc, label):
+    q, k, v = inputs_for(desc, "bf16", seed=3)
+    _, got, _, _ = run(lib, desc, q, k, v, out_dtype="bf16")
+    ref = oracle.attention(q, k, v, desc)
+    assert_close(got, ref, fp32=False, label=label + "/bf16-out")
+
+
+FP32_CASES = [
+    (Desc(4, 8, 8, 2, sigma=4, diag=True, mean=True), "tiny-workload"),
+    (Desc(4, 8, 8, 2, sigma=4, diag=True, mean=True, ref_dense=False), "tiny-pi3"),
+    (Desc(4, 8, 8, 2, sigma=4, diag=True, mean=True, mean_count=True), "tiny-count"),
+    (Desc(3, 5, 7, 2, sigma=1), "fp32-dense"),
+    (Desc(3, 9, 9, 2, g2f=True), "fp32-g2f"),
+    (Desc(3, 6, 7, 2, sigma=9, diag=True, mean=True), "fp32-sga9"),
+]
+
+
+@pytest.mark.parametrize("desc,label", FP32_CASES, ids=[c[1] for c in FP32_CASES])
+def test_parity_fp32(lib, desc, label):
+    q, k, v = inputs_for(desc, "fp32", seed=0)
+    _, got, _, _ = run(lib, desc, q, k, v, out_dtype="fp32", in_dtype="fp32")
+    ref = oracle.attention(q, k, v, desc)
+    print(label, "max-abs %.3e rel-L2 %.3e" % errors(got, ref))
+    assert_close(got, ref, fp32=True, label=label)
+
+
+@pytest.mark.parametrize("desc,label", [c for c in CASES if not c[0].g2f], ids=[c[1] for c in CASES if not c[0].g2f])
+def test_index_set_bit_exact(lib, desc, label):
+    q, k, v = inputs_for(desc, "bf16", seed=1)
+    plan, _, ws, _ = run(lib, desc, q, k, v)
+    idx, dcount = plan.index_set(ws)
+    assert np.array_equal(idx, oracle.index_set(desc))
+    assert np.array_equal(dcount, oracle.dropped_counts(desc).astype(np.int32))
+
+
+def key_at(p):
+    """Packed value-tile position -> key within the 64-key tile (the documented layout)."""
+    half, g, j = p >> 5, (p >> 3) & 3, p & 7
+    return half * 32 + (g * 4 + j if j < 4 else 16 + g * 4 + (j - 4))
+
+
+@pytest.mark.parametrize("desc,label", [CASES[3], CASES[5], CASES[6], CASES[7]], ids=["sga4", "sga9-pi3", "g2f", "sga4-37"])
+def test_packed_rows(lib, desc, label):
+    """Rows of S are bit-exact copies; the means are within one bf16 step of the fp64 means;
+    padding is zero; values sit in the key-minor tile order."""
+    import torch
+    q, k, v = inputs_for(desc, "bf16", seed=2)
+    plan, _, ws, _ = run(lib, desc, q, k, v)
+    lay = plan.layout()
+    H, d = desc.heads, desc.head_dim
+    rows = lay["segments"] * lay["segment_rows"]
+    kp = ws[lay["off_kpack"]:lay["off_kpack"] + H * rows * d * 2].view(torch.int16).cpu().numpy().view(np.uint16)
+    vp = ws[lay["off_vpack"]:lay["off_vpack"] + H * rows * d * 2].view(torch.int16).cpu().numpy().view(np.uint16)
+    kp = kp.reshape(H, rows, d)
+    perm = np.array([key_at(p) for p in range(64)])
+    vt = vp.reshape(H, rows // 64, d, 64)
+    vrows = np.zeros((H, rows // 64, 64, d), dtype=np.uint16)
+    vrows[:, :, perm, :] = vt.transpose(0, 1, 3, 2)
+    vrows = vrows.reshape(H, rows, d)
+    if desc.g2f:
+        for f in range(desc.frames):
+            seg = slice(f * lay["segment_rows"], f * lay["segment_rows"] + desc.L)
+            tok = slice(f * desc.L, (f + 1) * desc.L)
+            assert np.array_equal(kp[:, seg], k[:, tok]) and np.array_equal(vrows[:, seg], v[:, tok])
+            pad = slice(f * lay["segment_rows"] + desc.L, (f + 1) * lay["segment_rows"])
+            assert not kp[:, pad].any() and not vrows[:, pad].any()
+        return
+    S = oracle.index_set(desc)
+    nS = S.size
+    assert np.array_equal(kp[:, :nS], k[:, S]) and np.array_equal(vrows[:, :nS], v[:, S])
+    kbar, vbar, _, _ = oracle.frame_means(k, v, desc)
+    M = kbar.shape[1]
+    from synth import bf16_bits_to_f32
+    for got, ref in ((kp[:, nS:nS + M], kbar), (vrows[:, nS:nS + M], vbar)):
+        g = bf16_bits_to_f32(got).astype(np.float64)
+        assert np.all(np.abs(g - ref) <= np.abs(ref) * 2.0 ** -7 + 1e-6)
+    assert not kp[:, nS + M:].any() and not vrows[:, nS + M:].any()
+
+
+@pytest.mark.parametrize("desc,label", [CASES[4], CASES[5], CASES[6]], ids=["sga6-count", "sga9-pi3", "g2f"])
+def test_v_ones_gives_ones(lib, desc, label):
+    q, k, _ = inputs_for(desc, "bf16", seed=5)
+    v = np.full(q.shape, 0x3F80, dtype=np.uint16)  # bf16 1.0
+    _, got, _, _ = run(lib, desc, q, k, v)
+    assert np.max(np.abs(got - 1.0)) <= 4e-3
+
+
+def test_deterministic_and_poisoned_workspace(lib):
+    import torch
+    desc = CASES[7][0]
+    q, k, v = inputs_for(desc, "bf16", seed=6)
+    plan = lib.Plan(**plan_kwargs(desc))
+    qd, kd, vd = to_device(q), to_device(k), to_device(v)
+    ws = plan.new_workspace()
+    o1, o2, o3 = plan.new_output(), plan.new_output(), plan.new_output()
+    ws.zero_()
+    plan.forward(qd, kd, vd, o1, ws)
+    plan.forward(qd, kd, vd, o2, ws)
+    ws.fill_(0xFF)  # every bf16 lane becomes NaN
+    plan.forward(qd, kd, vd, o3, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(o1, o3)
+
+
+def test_pack_then_attend_equals_forward(lib):
+    import torch
+    desc = CASES[4][0]
+    q, k, v = inputs_for(desc, "bf16", seed=7)
+    plan = lib.Plan(**plan_kwargs(desc))
+    qd, kd, vd = to_device(q), to_device(k), to_device(v)
+    ws = plan.new_workspace()
+    o1, o2 = plan.new_output(), plan.new_output()
+    plan.forward(qd, kd, vd, o1, ws)
+    plan.pack(kd, vd, ws)
+    plan.attend(qd, kd, vd, o2, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+
+
+def test_error_codes(lib):
+    import torch
+    L = lib.lib()
+    desc = CASES[3][0]
+    plan = lib.Plan(**plan_kwargs(desc))
+    q, k, v = (to_device(x) for x in inputs_for(desc, "bf16", seed=8))
+    out = plan.new_output()
+    ws = plan.new_workspace()
+    nbytes = plan.workspace_bytes
+    stream = torch.cuda.current_stream().cuda_stream
+    h = plan.handle
+    P = lambda t, off=0: ctypes.c_void_p(t.data_ptr() + off)
+    assert L.vggt_attn_forward(h, P(q), P(k), P(v), P(out), P(ws), nbytes - 1, stream) == -3
+    assert L.vggt_attn_forward(h, P(q), P(k), P(v), P(out), None, nbytes, stream) == -1
+    assert L.vggt_attn_forward(h, None, P(k), P(v), P(out), P(ws), nbytes, stream) == -1
+    assert L.vggt_attn_forward(h, P(q, 2), P(k), P(v), P(out), P(ws), nbytes, stream) == -4
+    assert L.vggt_attn_forward(h, P(q), P(k), P(v), P(ws, 4096), P(ws), nbytes, stream) == -5
+    assert L.vggt_attn_forward(h, P(q), P(k), P(v), P(k), P(ws), nbytes, stream) == -5
+    assert b"overlaps" in L.vggt_attn_last_error()
+    assert L.vggt_attn_forward(None, P(q), P(k), P(v), P(out), P(ws), nbytes, stream) == -1
+    assert L.vggt_attn_forward(h, P(q), P(k), P(v), P(out), P(ws), nbytes, stream) == 0
+    assert L.vggt_attn_last_error() == b""
+    torch.cuda.synchronize()

@@ -1,0 +1,216 @@
+"""ctypes binding over libvggt_attn.so (the C ABI in include/vggt_attn.h).
+
+Argument marshalling only: every step of the computation runs in the library's HIP kernels.
+torch supplies device memory and the stream; nothing here computes attention.  If the shared
+library is missing, every call raises -- there is no fallback path."""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libvggt_attn.so")
+
+BF16, FP32 = 0, 1
+G2F, REF_DENSE, DIAG, MEAN, MEAN_COUNT = 1, 2, 4, 8, 16
+
+STATUS = {0: "OK", -1: "EINVAL", -2: "EUNSUPPORTED", -3: "ENOSPC", -4: "EALIGN", -5: "EALIAS", -6: "EHIP"}
+
+EXPORTS = ("vggt_attn_plan", "vggt_attn_plan_destroy", "vggt_attn_workspace_bytes", "vggt_attn_counts",
+           "vggt_attn_layout", "vggt_attn_forward", "vggt_attn_pack", "vggt_attn_attend",
+           "vggt_attn_copy_index_set", "vggt_attn_last_error")
+
+
+class VggtAttnError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"{STATUS.get(code, code)}: {message}")
+        self.code = code
+        self.status = STATUS.get(code, str(code))
+
+
+class Layout(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_int64) for name in (
+        "segments", "segment_rows", "keys_per_segment", "off_index", "off_dcount", "off_means",
+        "off_kpack", "off_vpack", "total_bytes")]
+
+    def as_dict(self) -> dict:
+        return {name: int(getattr(self, name)) for name, _ in self._fields_}
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load the shared library (once); raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m vggt_global_attention_attn_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i64p = ctypes.c_void_p, ctypes.POINTER(ctypes.c_int64)
+    L.vggt_attn_plan.argtypes = [ctypes.POINTER(vp)] + [ctypes.c_int] * 7 + [ctypes.c_uint, ctypes.c_int, ctypes.c_int]
+    L.vggt_attn_plan.restype = ctypes.c_int
+    L.vggt_attn_plan_destroy.argtypes = [vp]
+    L.vggt_attn_plan_destroy.restype = None
+    L.vggt_attn_workspace_bytes.argtypes = [vp]
+    L.vggt_attn_workspace_bytes.restype = ctypes.c_size_t
+    L.vggt_attn_counts.argtypes = [vp, i64p, i64p, i64p, ctypes.POINTER(ctypes.c_double)]
+    L.vggt_attn_counts.restype = ctypes.c_int
+    L.vggt_attn_layout.argtypes = [vp, ctypes.POINTER(Layout)]
+    L.vggt_attn_layout.restype = ctypes.c_int
+    L.vggt_attn_forward.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    L.vggt_attn_forward.restype = ctypes.c_int
+    L.vggt_attn_pack.argtypes = [vp, vp, vp, vp, ctypes.c_size_t, vp]
+    L.vggt_attn_pack.restype = ctypes.c_int
+    L.vggt_attn_attend.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    L.vggt_attn_attend.restype = ctypes.c_int
+    L.vggt_attn_copy_index_set.argtypes = [vp, vp, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32), vp]
+    L.vggt_attn_copy_index_set.restype = ctypes.c_int
+    L.vggt_attn_last_error.argtypes = []
+    L.vggt_attn_last_error.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def _check(rc: int) -> None:
+    if rc != 0:
+        raise VggtAttnError(rc, lib().vggt_attn_last_error().decode())
+
+
+def _dtype_code(name: str) -> int:
+    if name in ("bf16", "bfloat16"):
+        return BF16
+    if name in ("fp32", "float32"):
+        return FP32
+    raise ValueError(f"dtype must be 'bf16' or 'fp32', got {name!r}")
+
+
+def _stream_handle(stream, device=None):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream(device).cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _ptr(t) -> int:
+    return 0 if t is None else int(t.data_ptr())
+
+
+class Plan:
+    """An immutable description of one global-attention call (see include/vggt_attn.h)."""
+
+    def __init__(self, frames: int, grid_h: int, grid_w: int, heads: int, head_dim: int = 64,
+                 n_special: int = 5, sigma: int = 1, ref_dense: bool = True, diag: bool = False,
+                 mean: bool = False, mean_count: bool = False, g2f: bool = False,
+                 in_dtype: str = "bf16", out_dtype: str = "fp32", flags: int | None = None):
+        if flags is None:
+            flags = ((G2F if g2f else 0) | (REF_DENSE if ref_dense else 0) | (DIAG if diag else 0) |
+                     (MEAN if mean else 0) | (MEAN_COUNT if mean_count else 0))
+        self._h = ctypes.c_void_p()
+        self.frames, self.grid_h, self.grid_w, self.heads, self.head_dim = frames, grid_h, grid_w, heads, head_dim
+        self.n_special, self.sigma, self.flags = n_special, sigma, flags
+        self.in_dtype, self.out_dtype = in_dtype, out_dtype
+        _check(lib().vggt_attn_plan(ctypes.byref(self._h), frames, grid_h, grid_w, n_special, heads, head_dim,
+                                    sigma, flags, _dtype_code(in_dtype), _dtype_code(out_dtype)))
+        self.L = n_special + grid_h * grid_w
+        self.T = frames * self.L
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value and _lib is not None:
+            _lib.vggt_attn_plan_destroy(h)
+            self._h = None
+
+    @property
+    def handle(self) -> ctypes.c_void_p:
+        return self._h
+
+    @property
+    def workspace_bytes(self) -> int:
+        return int(lib().vggt_attn_workspace_bytes(self._h))
+
+    def counts(self) -> dict:
+        n_kv, n_mean, n_diag = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+        flops = ctypes.c_double()
+        _check(lib().vggt_attn_counts(self._h, ctypes.byref(n_kv), ctypes.byref(n_mean), ctypes.byref(n_diag),
+                                      ctypes.byref(flops)))
+        return {"n_kv": n_kv.value, "n_mean": n_mean.value, "n_diag": n_diag.value, "flops": flops.value}
+
+    def layout(self) -> dict:
+        lay = Layout()
+        _check(lib().vggt_attn_layout(self._h, ctypes.byref(lay)))
+        return lay.as_dict()
+
+    # -- device calls (torch tensors for memory, a torch stream or raw handle for ordering) --
+
+    def _check_tensor(self, t, name: str, dtype_name: str) -> None:
+        import torch
+        want = torch.bfloat16 if dtype_name == "bf16" else torch.float32
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if t.dtype != want:
+            raise ValueError(f"{name} must be {want}, got {t.dtype}")
+        if tuple(t.shape) != (self.heads, self.T, self.head_dim) or not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous [{self.heads}, {self.T}, {self.head_dim}], got {tuple(t.shape)}")
+
+    def _check_ws(self, ws) -> None:
+        if not ws.is_cuda or not ws.is_contiguous():
+            raise ValueError("workspace must be a contiguous GPU tensor")
+
+    def new_workspace(self, device="cuda"):
+        import torch
+        return torch.empty(max(1, self.workspace_bytes), dtype=torch.uint8, device=device)
+
+    def new_output(self, device="cuda"):
+        import torch
+        dt = torch.bfloat16 if self.out_dtype == "bf16" else torch.float32
+        return torch.empty((self.heads, self.T, self.head_dim), dtype=dt, device=device)
+
+    def forward(self, q, k, v, out, workspace, stream=None) -> None:
+        for t, n in ((q, "q"), (k, "k"), (v, "v")):
+            self._check_tensor(t, n, self.in_dtype)
+        self._check_tensor(out, "out", self.out_dtype)
+        self._check_ws(workspace)
+        _check(lib().vggt_attn_forward(self._h, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(workspace),
+                                       workspace.numel() * workspace.element_size(),
+                                       _stream_handle(stream, q.device)))
+
+    def pack(self, k, v, workspace, stream=None) -> None:
+        for t, n in ((k, "k"), (v, "v")):
+            self._check_tensor(t, n, self.in_dtype)
+        self._check_ws(workspace)
+        _check(lib().vggt_attn_pack(self._h, _ptr(k), _ptr(v), _ptr(workspace),
+                                    workspace.numel() * workspace.element_size(), _stream_handle(stream, k.device)))
+
+    def attend(self, q, k, v, out, workspace, stream=None) -> None:
+        for t, n in ((q, "q"), (k, "k"), (v, "v")):
+            self._check_tensor(t, n, self.in_dtype)
+        self._check_tensor(out, "out", self.out_dtype)
+        self._check_ws(workspace)
+        _check(lib().vggt_attn_attend(self._h, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(workspace),
+                                      workspace.numel() * workspace.element_size(),
+                                      _stream_handle(stream, q.device)))
+
+    def index_set(self, workspace, stream=None):
+        """(S as int32 token ids, |D_f| per frame) copied from a packed workspace."""
+        c = self.counts()
+        g2f = bool(self.flags & G2F)
+        idx = np.zeros(0 if g2f else c["n_kv"], dtype=np.int32)
+        dcount = np.zeros(self.frames, dtype=np.int32)
+        i32p = ctypes.POINTER(ctypes.c_int32)
+        _check(lib().vggt_attn_copy_index_set(
+            self._h, _ptr(workspace), idx.ctypes.data_as(i32p) if idx.size else None,
+            dcount.ctypes.data_as(i32p), _stream_handle(stream, workspace.device)))
+        return idx, dcount
+
+
+def attention(q, k, v, plan: Plan, stream=None):
+    """Allocate out and a workspace with torch, run one forward, return out."""
+    out = plan.new_output(q.device)
+    ws = plan.new_workspace(q.device)
+    plan.forward(q, k, v, out, ws, stream)
+    return out

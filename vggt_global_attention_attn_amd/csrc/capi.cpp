@@ -1,0 +1,186 @@
+// C ABI entry points: argument checks, then kernel launches on the caller's stream.
+#include <hip/hip_runtime_api.h>
+
+#include <cstdint>
+#include <cstdio>
+#include <new>
+#include <string>
+
+#include "launch.h"
+#include "plan.h"
+#include "vggt_attn.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int set_error(int code, const std::string& msg) {
+  g_last_error = msg;
+  return code;
+}
+
+int ok() {
+  g_last_error.clear();
+  return VGGT_ATTN_OK;
+}
+
+int hip_error(hipError_t e, const char* what) {
+  return set_error(VGGT_ATTN_EHIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+bool misaligned(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) != 0; }
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return na && nb && x < y + nb && y < x + na;
+}
+
+size_t tensor_bytes(const vggt_attn_plan_s& p, int dtype) {
+  return size_t(p.heads) * size_t(p.T) * size_t(p.head_dim) * (dtype == VGGT_ATTN_BF16 ? 2 : 4);
+}
+
+int check_workspace(const vggt_attn_plan_s& p, const void* ws, size_t ws_bytes) {
+  if (!ws) return set_error(VGGT_ATTN_EINVAL, "workspace is NULL");
+  if (misaligned(ws)) return set_error(VGGT_ATTN_EALIGN, "workspace is not 16-byte aligned");
+  if (ws_bytes < size_t(p.layout.total_bytes))
+    return set_error(VGGT_ATTN_ENOSPC, "workspace has " + std::to_string(ws_bytes) + " bytes, needs " +
+                                           std::to_string(p.layout.total_bytes));
+  return VGGT_ATTN_OK;
+}
+
+int check_tensors(const vggt_attn_plan_s& p, const void* q, const void* k, const void* v,
+                  const void* out, bool need_q_out) {
+  if (!k || !v || (need_q_out && (!q || !out))) return set_error(VGGT_ATTN_EINVAL, "NULL tensor pointer");
+  if (misaligned(k) || misaligned(v) || (need_q_out && (misaligned(q) || misaligned(out))))
+    return set_error(VGGT_ATTN_EALIGN, "tensor pointer is not 16-byte aligned");
+  return VGGT_ATTN_OK;
+}
+
+int check_out_alias(const vggt_attn_plan_s& p, const void* q, const void* k, const void* v,
+                    const void* out, const void* ws, size_t ws_bytes) {
+  const size_t nin = tensor_bytes(p, p.in_dtype), nout = tensor_bytes(p, p.out_dtype);
+  if (overlaps(out, nout, q, nin) || overlaps(out, nout, k, nin) || overlaps(out, nout, v, nin) ||
+      overlaps(out, nout, ws, ws_bytes))
+    return set_error(VGGT_ATTN_EALIAS, "out overlaps q, k, v or the workspace");
+  return VGGT_ATTN_OK;
+}
+
+int do_pack(const vggt_attn_plan_s& p, const void* k, const void* v, void* ws, hipStream_t s) {
+  hipError_t e = vggt::launch_means(p, k, v, ws, s);
+  if (e != hipSuccess) return hip_error(e, "means kernel launch");
+  e = vggt::launch_pack(p, k, v, ws, s);
+  if (e != hipSuccess) return hip_error(e, "pack kernel launch");
+  return VGGT_ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int vggt_attn_plan(vggt_attn_plan_t** out, int frames, int grid_h, int grid_w, int n_special,
+                   int heads, int head_dim, int sigma, unsigned flags, int in_dtype,
+                   int out_dtype) {
+  if (!out) return set_error(VGGT_ATTN_EINVAL, "plan output pointer is NULL");
+  *out = nullptr;
+  auto* p = new (std::nothrow) vggt_attn_plan_s();
+  if (!p) return set_error(VGGT_ATTN_EINVAL, "out of host memory");
+  std::string err;
+  const int rc = vggt::build_plan(p, frames, grid_h, grid_w, n_special, heads, head_dim, sigma,
+                                  flags, in_dtype, out_dtype, &err);
+  if (rc != VGGT_ATTN_OK) {
+    delete p;
+    return set_error(rc, err);
+  }
+  *out = p;
+  return ok();
+}
+
+void vggt_attn_plan_destroy(vggt_attn_plan_t* plan) { delete plan; }
+
+size_t vggt_attn_workspace_bytes(const vggt_attn_plan_t* plan) {
+  return plan ? size_t(plan->layout.total_bytes) : 0;
+}
+
+int vggt_attn_counts(const vggt_attn_plan_t* plan, int64_t* n_kv, int64_t* n_mean,
+                     int64_t* n_diag, double* flops) {
+  if (!plan) return set_error(VGGT_ATTN_EINVAL, "plan is NULL");
+  if (n_kv) *n_kv = plan->g2f ? plan->L : plan->nS;
+  if (n_mean) *n_mean = plan->M;
+  if (n_diag) *n_diag = plan->n_diag;
+  if (flops) *flops = plan->flops;
+  return ok();
+}
+
+int vggt_attn_layout(const vggt_attn_plan_t* plan, vggt_attn_layout_t* out) {
+  if (!plan || !out) return set_error(VGGT_ATTN_EINVAL, "NULL argument");
+  *out = plan->layout;
+  return ok();
+}
+
+int vggt_attn_pack(const vggt_attn_plan_t* plan, const void* k, const void* v, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  if (!plan) return set_error(VGGT_ATTN_EINVAL, "plan is NULL");
+  int rc = check_tensors(*plan, nullptr, k, v, nullptr, false);
+  if (rc) return rc;
+  if ((rc = check_workspace(*plan, workspace, workspace_bytes))) return rc;
+  const size_t nin = tensor_bytes(*plan, plan->in_dtype);
+  if (overlaps(workspace, workspace_bytes, k, nin) || overlaps(workspace, workspace_bytes, v, nin))
+    return set_error(VGGT_ATTN_EALIAS, "workspace overlaps k or v");
+  if ((rc = do_pack(*plan, k, v, workspace, static_cast<hipStream_t>(stream)))) return rc;
+  return ok();
+}
+
+int vggt_attn_attend(const vggt_attn_plan_t* plan, const void* q, const void* k, const void* v,
+                     void* out, const void* workspace, size_t workspace_bytes, void* stream) {
+  if (!plan) return set_error(VGGT_ATTN_EINVAL, "plan is NULL");
+  int rc = check_tensors(*plan, q, k, v, out, true);
+  if (rc) return rc;
+  if ((rc = check_workspace(*plan, workspace, workspace_bytes))) return rc;
+  if ((rc = check_out_alias(*plan, q, k, v, out, workspace, workspace_bytes))) return rc;
+  hipError_t e = vggt::launch_attend(*plan, q, k, v, out, workspace, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_error(e, "attention kernel launch");
+  return ok();
+}
+
+int vggt_attn_forward(const vggt_attn_plan_t* plan, const void* q, const void* k, const void* v,
+                      void* out, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!plan) return set_error(VGGT_ATTN_EINVAL, "plan is NULL");
+  int rc = check_tensors(*plan, q, k, v, out, true);
+  if (rc) return rc;
+  if ((rc = check_workspace(*plan, workspace, workspace_bytes))) return rc;
+  if ((rc = check_out_alias(*plan, q, k, v, out, workspace, workspace_bytes))) return rc;
+  const size_t nin = tensor_bytes(*plan, plan->in_dtype);
+  if (overlaps(workspace, workspace_bytes, k, nin) || overlaps(workspace, workspace_bytes, v, nin) ||
+      overlaps(workspace, workspace_bytes, q, nin))
+    return set_error(VGGT_ATTN_EALIAS, "workspace overlaps q, k or v");
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((rc = do_pack(*plan, k, v, workspace, s))) return rc;
+  hipError_t e = vggt::launch_attend(*plan, q, k, v, out, workspace, s);
+  if (e != hipSuccess) return hip_error(e, "attention kernel launch");
+  return ok();
+}
+
+int vggt_attn_copy_index_set(const vggt_attn_plan_t* plan, const void* workspace,
+                             int32_t* host_idx, int32_t* host_dcount, void* stream) {
+  if (!plan || !workspace) return set_error(VGGT_ATTN_EINVAL, "NULL argument");
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const char* base = static_cast<const char*>(workspace);
+  hipError_t e;
+  if (host_idx && !plan->g2f && plan->nS > 0) {
+    e = hipMemcpyAsync(host_idx, base + plan->layout.off_index, size_t(plan->nS) * 4,
+                       hipMemcpyDeviceToHost, s);
+    if (e != hipSuccess) return hip_error(e, "index copy");
+  }
+  if (host_dcount) {
+    e = hipMemcpyAsync(host_dcount, base + plan->layout.off_dcount, size_t(plan->frames) * 4,
+                       hipMemcpyDeviceToHost, s);
+    if (e != hipSuccess) return hip_error(e, "dcount copy");
+  }
+  e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_error(e, "stream synchronize");
+  return ok();
+}
+
+const char* vggt_attn_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,23 @@
+// Kernel launchers (defined in the .hip files) used by the C ABI.  Each enqueues on `stream`
+// and returns the hipError_t of the launch.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+
+#include "plan.h"
+
+namespace vggt {
+
+// Mean key/value of the dropped patches of every compressed frame -> workspace means area.
+hipError_t launch_means(const vggt_attn_plan_s& p, const void* k, const void* v, void* ws,
+                        hipStream_t stream);
+
+// S, |D_f|, and the packed key/value tiles -> workspace.  Runs after launch_means.
+hipError_t launch_pack(const vggt_attn_plan_s& p, const void* k, const void* v, void* ws,
+                       hipStream_t stream);
+
+// Attention over the packed keys (bf16 inputs: MFMA kernel; fp32 inputs: fp32 kernel).
+hipError_t launch_attend(const vggt_attn_plan_s& p, const void* q, const void* k, const void* v,
+                         void* out, const void* ws, hipStream_t stream);
+
+}  // namespace vggt

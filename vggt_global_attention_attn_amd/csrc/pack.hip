@@ -1,0 +1,240 @@
+// Gather/pack stage of subsampled global attention on gfx950.
+//
+// "AVGGT: Rethinking Global Attention for Accelerating VGGT" (papernotes.org CVPR 2026 notes),
+// 关键设计 2: the keys and values of the global layer are restricted to S; 关键设计 3: one mean
+// key/value stands in for the dropped patches.  Both kernels are HBM-bound streaming passes.
+//
+//   means_kernel  one work-group per (compressed frame, head): float32 sums of the frame's
+//                 dropped K and V rows (16-byte loads, 32 rows in flight per work-group),
+//                 divided by |D_f| and rounded to the input type.
+//   pack_kernel   one work-group per (64-row key tile, head): copies the K/V rows of S (and
+//                 the means, then zero padding) into packed tiles.  Keys stay row-major
+//                 [row][d]; for bf16 the values are written as [d][64] key-minor tiles in the
+//                 order the PV matrix-core step reads them, so the attention kernel loads
+//                 every operand with contiguous 16-byte reads.  Head 0 also exports S, and
+//                 work-group (0,0) exports |D_f|.
+#include <hip/hip_runtime.h>
+
+#include "device_common.h"
+#include "launch.h"
+
+namespace vggt {
+namespace {
+
+struct MeansArgs {
+  const void* k;
+  const void* v;
+  void* means;  // [H][M][2][64]
+  int64_t T;
+  int M;
+  int dropped;
+  IndexGeom g;
+};
+
+template <typename E>
+__device__ __forceinline__ void add_chunk(float* acc, const uint4& raw);
+
+template <>
+__device__ __forceinline__ void add_chunk<uint16_t>(float* acc, const uint4& raw) {
+  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    acc[2 * i] += __uint_as_float(w[i] << 16);
+    acc[2 * i + 1] += __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+
+template <>
+__device__ __forceinline__ void add_chunk<float>(float* acc, const uint4& raw) {
+  acc[0] += __uint_as_float(raw.x);
+  acc[1] += __uint_as_float(raw.y);
+  acc[2] += __uint_as_float(raw.z);
+  acc[3] += __uint_as_float(raw.w);
+}
+
+__device__ __forceinline__ void store_elem(uint16_t* p, float x) { *p = f32_to_bf16(x); }
+__device__ __forceinline__ void store_elem(float* p, float x) { *p = x; }
+
+template <typename E>
+__global__ __launch_bounds__(256) void means_kernel(MeansArgs a) {
+  constexpr int CH = 16 / int(sizeof(E));  // channels per 16-byte chunk
+  constexpr int CPR = kHeadDim / CH;       // chunks per row
+  constexpr int RG = 256 / CPR;            // rows in flight
+  const int m = blockIdx.x, h = blockIdx.y;
+  const int f = a.g.ref_dense ? m + 1 : m;
+  const int tid = threadIdx.x, chunk = tid % CPR, rg = tid / CPR;
+  const size_t base = (size_t(h) * size_t(a.T) + size_t(f) * a.g.L + a.g.n_special) * kHeadDim + chunk * CH;
+  const E* kb = static_cast<const E*>(a.k) + base;
+  const E* vb = static_cast<const E*>(a.v) + base;
+  float ks[CH], vs[CH];
+#pragma unroll
+  for (int i = 0; i < CH; ++i) ks[i] = vs[i] = 0.f;
+  for (int p = rg; p < a.g.P; p += RG) {
+    const int r = p / a.g.grid_w, c = p - r * a.g.grid_w;
+    if ((r % a.g.s_h) == 0 && (c % a.g.s_w) == 0) continue;  // kept: not part of D_f
+    add_chunk<E>(ks, *reinterpret_cast<const uint4*>(kb + size_t(p) * kHeadDim));
+    add_chunk<E>(vs, *reinterpret_cast<const uint4*>(vb + size_t(p) * kHeadDim));
+  }
+  __shared__ float red[RG][2][kHeadDim];
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+    red[rg][0][chunk * CH + i] = ks[i];
+    red[rg][1][chunk * CH + i] = vs[i];
+  }
+  __syncthreads();
+  if (tid < 2 * kHeadDim) {
+    const int which = tid / kHeadDim, ch = tid % kHeadDim;
+    float s = 0.f;
+    for (int r = 0; r < RG; ++r) s += red[r][which][ch];
+    E* dst = static_cast<E*>(a.means) + ((size_t(h) * a.M + m) * 2 + which) * kHeadDim + ch;
+    store_elem(dst, s / float(a.dropped));
+  }
+}
+
+struct PackArgs {
+  const void* k;
+  const void* v;
+  const void* means;  // [H][M][2][64]
+  void* kpack;        // [H][rows][64]
+  void* vpack;        // bf16: [H][rows/64][64][64] key-minor; fp32: [H][rows][64]
+  int32_t* index;     // [|S|] or nullptr
+  int32_t* dcount;    // [N]
+  int64_t T;
+  int64_t rows_per_head;
+  int64_t nS;
+  int M;
+  int g2f;
+  int segment_rows;
+  int frames;
+  int dropped;
+  IndexGeom g;
+};
+
+// Where packed row `row` of a head comes from: a token (>= 0), mean `-2 - m`, or padding (-1).
+__device__ __forceinline__ int64_t packed_source(const PackArgs& a, int64_t row) {
+  if (a.g2f) {
+    const int64_t f = row / a.segment_rows, j = row - f * a.segment_rows;
+    return j < a.g.L ? f * a.g.L + j : -1;
+  }
+  if (row < a.nS) return token_of_kept_index(a.g, row);
+  if (row < a.nS + a.M) return -2 - (row - a.nS);
+  return -1;
+}
+
+// Position p (0..63) of a packed value tile holds key key_at(p): within each half of 32 keys,
+// positions g*8 + j hold keys g*4 + j (j < 4) and 16 + g*4 + (j - 4) (j >= 4).  This is the
+// order in which a 16x16 score block leaves the matrix core (lane group g owns keys g*4..g*4+3
+// of every 16-key block), so P can feed the PV product straight from registers.
+__device__ __forceinline__ int key_at(int p) {
+  const int half = p >> 5, g = (p >> 3) & 3, j = p & 7;
+  return half * 32 + (j < 4 ? g * 4 + j : 16 + g * 4 + (j - 4));
+}
+
+template <typename E, bool TRANSPOSE_V>
+__global__ __launch_bounds__(256) void pack_kernel(PackArgs a) {
+  constexpr int CH = 16 / int(sizeof(E));
+  constexpr int CPR = kHeadDim / CH;
+  constexpr int CHUNKS = kTile * CPR;
+  const int tile = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  const E* K = static_cast<const E*>(a.k) + size_t(h) * size_t(a.T) * kHeadDim;
+  const E* V = static_cast<const E*>(a.v) + size_t(h) * size_t(a.T) * kHeadDim;
+  const E* MK = static_cast<const E*>(a.means) + size_t(h) * a.M * 2 * kHeadDim;
+  E* KP = static_cast<E*>(a.kpack) + (size_t(h) * a.rows_per_head + size_t(tile) * kTile) * kHeadDim;
+  E* VP = static_cast<E*>(a.vpack) + (size_t(h) * a.rows_per_head + size_t(tile) * kTile) * kHeadDim;
+  // V rows of the tile, padded to 68 halves per row for conflict-light column reads.
+  __shared__ uint16_t vt[TRANSPOSE_V ? kTile : 1][68];
+  for (int e = tid; e < CHUNKS; e += 256) {
+    const int row = e / CPR, ch = e % CPR;
+    const int64_t prow = int64_t(tile) * kTile + row;
+    const int64_t src = packed_source(a, prow);
+    uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
+    if (src >= 0) {
+      kv = *reinterpret_cast<const uint4*>(K + size_t(src) * kHeadDim + ch * CH);
+      vv = *reinterpret_cast<const uint4*>(V + size_t(src) * kHeadDim + ch * CH);
+      if (a.index && h == 0 && ch == 0 && prow < a.nS) a.index[prow] = int32_t(src);
+    } else if (src <= -2) {
+      const int64_t m = -2 - src;
+      kv = *reinterpret_cast<const uint4*>(MK + (size_t(m) * 2 + 0) * kHeadDim + ch * CH);
+      vv = *reinterpret_cast<const uint4*>(MK + (size_t(m) * 2 + 1) * kHeadDim + ch * CH);
+    }
+    *reinterpret_cast<uint4*>(KP + size_t(row) * kHeadDim + ch * CH) = kv;
+    if constexpr (TRANSPOSE_V) {
+      uint2* dst = reinterpret_cast<uint2*>(&vt[row][ch * CH]);
+      dst[0] = make_uint2(vv.x, vv.y);
+      dst[1] = make_uint2(vv.z, vv.w);
+    } else {
+      *reinterpret_cast<uint4*>(VP + size_t(row) * kHeadDim + ch * CH) = vv;
+    }
+  }
+  if (a.dcount && h == 0 && tile == 0) {
+    for (int f = tid; f < a.frames; f += 256)
+      a.dcount[f] = (a.g.subsampled && !(a.g.ref_dense && f == 0)) ? a.dropped : 0;
+  }
+  if constexpr (TRANSPOSE_V) {
+    __syncthreads();
+    // Output tile [64 d][64 positions]: thread writes 8 positions (16 bytes) of one d-row.
+    for (int e = tid; e < kTile * 8; e += 256) {
+      const int pc = e & 7, d = e >> 3;
+      uint32_t w[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t lo = vt[key_at(pc * 8 + 2 * i)][d];
+        const uint32_t hi = vt[key_at(pc * 8 + 2 * i + 1)][d];
+        w[i] = lo | (hi << 16);
+      }
+      *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(VP) + d * kTile + pc * 8) =
+          make_uint4(w[0], w[1], w[2], w[3]);
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_means(const vggt_attn_plan_s& p, const void* k, const void* v, void* ws,
+                        hipStream_t stream) {
+  if (p.M == 0) return hipSuccess;
+  MeansArgs a{};
+  a.k = k;
+  a.v = v;
+  a.means = static_cast<char*>(ws) + p.layout.off_means;
+  a.T = p.T;
+  a.M = int(p.M);
+  a.dropped = int(p.dropped);
+  a.g = p.geom;
+  const dim3 grid(unsigned(p.M), unsigned(p.heads));
+  if (p.in_dtype == VGGT_ATTN_BF16)
+    hipLaunchKernelGGL(means_kernel<uint16_t>, grid, dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL(means_kernel<float>, grid, dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack(const vggt_attn_plan_s& p, const void* k, const void* v, void* ws,
+                       hipStream_t stream) {
+  char* base = static_cast<char*>(ws);
+  PackArgs a{};
+  a.k = k;
+  a.v = v;
+  a.means = base + p.layout.off_means;
+  a.kpack = base + p.layout.off_kpack;
+  a.vpack = base + p.layout.off_vpack;
+  a.index = p.g2f ? nullptr : reinterpret_cast<int32_t*>(base + p.layout.off_index);
+  a.dcount = reinterpret_cast<int32_t*>(base + p.layout.off_dcount);
+  a.T = p.T;
+  a.rows_per_head = p.rows_per_head;
+  a.nS = p.nS;
+  a.M = int(p.M);
+  a.g2f = p.g2f ? 1 : 0;
+  a.segment_rows = int(p.segment_rows);
+  a.frames = p.frames;
+  a.dropped = int(p.dropped);
+  a.g = p.geom;
+  const dim3 grid(unsigned(p.rows_per_head / kTile), unsigned(p.heads));
+  if (p.in_dtype == VGGT_ATTN_BF16)
+    hipLaunchKernelGGL((pack_kernel<uint16_t, true>), grid, dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL((pack_kernel<float, false>), grid, dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace vggt

@@ -1,0 +1,134 @@
+// Plan construction: validation, window shape, sizes of S / means / diagonal terms, FLOPs and
+// the workspace layout.
+//
+// Sources: "AVGGT: Rethinking Global Attention for Accelerating VGGT" (papernotes.org CVPR 2026
+// notes), 关键设计 1 (Global-to-Frame keeps the per-frame layout), 关键设计 2 (sigma = s_h*s_w
+// with 2->(1,2), 4->(2,2), 6->(2,3), 9->(3,3); the first patch of each window, all queries and
+// all special tokens kept; frame 0 uncompressed for VGGT, every frame compressed for pi^3),
+// 关键设计 3 (diagonal and mean terms); "RegimeVGGT ..." (papernotes.org NeurIPS 2026 notes),
+// 核心机制 (L = T + 5 tokens per frame).
+#include "plan.h"
+
+#include <cstdio>
+
+namespace vggt {
+namespace {
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+int64_t align256(int64_t x) { return (x + 255) & ~int64_t(255); }
+
+bool window_of(int sigma, int* s_h, int* s_w) {
+  switch (sigma) {
+    case 1: *s_h = 1; *s_w = 1; return true;
+    case 2: *s_h = 1; *s_w = 2; return true;
+    case 4: *s_h = 2; *s_w = 2; return true;
+    case 6: *s_h = 2; *s_w = 3; return true;
+    case 9: *s_h = 3; *s_w = 3; return true;
+    default: return false;
+  }
+}
+
+int fail(std::string* err, int code, const char* fmt, long long a = 0, long long b = 0) {
+  char buf[256];
+  std::snprintf(buf, sizeof buf, fmt, a, b);
+  if (err) *err = buf;
+  return code;
+}
+
+}  // namespace
+
+int build_plan(vggt_attn_plan_s* p, int frames, int grid_h, int grid_w, int n_special, int heads,
+               int head_dim, int sigma, unsigned flags, int in_dtype, int out_dtype,
+               std::string* err) {
+  if (frames < 1 || grid_h < 1 || grid_w < 1 || heads < 1 || n_special < 0)
+    return fail(err, VGGT_ATTN_EINVAL, "frames, grid_h, grid_w, heads must be >= 1 and n_special >= 0");
+  if (heads > kMaxHeads) return fail(err, VGGT_ATTN_EINVAL, "heads %lld exceeds %lld", heads, kMaxHeads);
+  if (head_dim != kHeadDim)
+    return fail(err, VGGT_ATTN_EUNSUPPORTED, "head_dim %lld not supported (only %lld)", head_dim, kHeadDim);
+  int s_h, s_w;
+  if (!window_of(sigma, &s_h, &s_w))
+    return fail(err, VGGT_ATTN_EINVAL, "sigma %lld not in {1, 2, 4, 6, 9}", sigma);
+  const unsigned known = VGGT_ATTN_G2F | VGGT_ATTN_REF_DENSE | VGGT_ATTN_DIAG | VGGT_ATTN_MEAN |
+                         VGGT_ATTN_MEAN_COUNT;
+  if (flags & ~known) return fail(err, VGGT_ATTN_EINVAL, "unknown flag bits 0x%llx", flags & ~known);
+  const bool g2f = flags & VGGT_ATTN_G2F;
+  if (g2f && (sigma != 1 || (flags & (VGGT_ATTN_DIAG | VGGT_ATTN_MEAN))))
+    return fail(err, VGGT_ATTN_EINVAL, "G2F takes sigma == 1 and no DIAG/MEAN");
+  const bool dtype_ok = (in_dtype == VGGT_ATTN_BF16 && (out_dtype == VGGT_ATTN_FP32 || out_dtype == VGGT_ATTN_BF16)) ||
+                        (in_dtype == VGGT_ATTN_FP32 && out_dtype == VGGT_ATTN_FP32);
+  if (!dtype_ok)
+    return fail(err, VGGT_ATTN_EINVAL, "dtype pair (%lld, %lld) not supported", in_dtype, out_dtype);
+
+  const int64_t P = int64_t(grid_h) * grid_w;
+  const int64_t L = P + n_special;
+  const int64_t T = L * frames;
+  if (P > (1 << 24) || T > kMaxTokens)
+    return fail(err, VGGT_ATTN_EINVAL, "T = %lld tokens exceeds the limit %lld", T, kMaxTokens);
+
+  *p = vggt_attn_plan_s{};
+  p->frames = frames; p->grid_h = grid_h; p->grid_w = grid_w; p->n_special = n_special;
+  p->heads = heads; p->head_dim = head_dim; p->sigma = sigma; p->flags = flags;
+  p->in_dtype = in_dtype; p->out_dtype = out_dtype;
+  p->g2f = g2f;
+  p->subsampled = sigma > 1;
+  p->ref_dense = flags & VGGT_ATTN_REF_DENSE;
+  p->diag = (flags & VGGT_ATTN_DIAG) && p->subsampled;
+  p->mean = (flags & VGGT_ATTN_MEAN) && p->subsampled;
+  p->mean_count = flags & VGGT_ATTN_MEAN_COUNT;
+  p->s_h = s_h; p->s_w = s_w;
+  p->L = int(L); p->P = int(P); p->T = T;
+  p->kh = int(ceil_div(grid_h, s_h));
+  p->kw = int(ceil_div(grid_w, s_w));
+  p->kept = p->kh * p->kw;                 // partial windows at the grid edge count
+  p->dropped = P - p->kept;
+
+  if (!p->subsampled) {
+    p->n_dense_frames = frames;
+    p->n_compressed_frames = 0;
+  } else {
+    p->n_dense_frames = p->ref_dense ? 1 : 0;
+    p->n_compressed_frames = frames - p->n_dense_frames;
+  }
+  // |S| = specials of every frame + every patch of dense frames + kept grid points elsewhere.
+  p->nS = int64_t(frames) * n_special + p->n_dense_frames * P + p->n_compressed_frames * p->kept;
+  p->M = (p->mean && p->dropped > 0) ? p->n_compressed_frames : 0;
+  p->n_diag = p->diag ? p->n_compressed_frames * p->dropped : 0;
+
+  const double d4H = 4.0 * head_dim * heads;
+  if (g2f) {
+    p->segments = frames;
+    p->keys_per_segment = L;
+    p->n_plain = L;
+    p->flops = d4H * double(frames) * double(L) * double(L);
+  } else {
+    p->segments = 1;
+    p->keys_per_segment = p->nS + p->M;
+    p->n_plain = p->nS;
+    p->flops = d4H * (double(T) * double(p->nS + p->M) + double(p->n_diag));
+  }
+  p->segment_rows = ceil_div(p->keys_per_segment, kTile) * kTile;
+  p->rows_per_head = p->segments * p->segment_rows;
+  if (p->rows_per_head > kMaxPackedRows)
+    return fail(err, VGGT_ATTN_EINVAL, "packed rows per head %lld exceed %lld", p->rows_per_head, kMaxPackedRows);
+
+  p->elem_bytes = in_dtype == VGGT_ATTN_BF16 ? 2 : 4;
+  vggt_attn_layout_t& lay = p->layout;
+  lay.segments = p->segments;
+  lay.segment_rows = p->segment_rows;
+  lay.keys_per_segment = p->keys_per_segment;
+  int64_t off = 0;
+  lay.off_index = off;  off = align256(off + (g2f ? 0 : p->nS) * 4);
+  lay.off_dcount = off; off = align256(off + int64_t(frames) * 4);
+  lay.off_means = off;  off = align256(off + int64_t(heads) * p->M * 2 * head_dim * int64_t(p->elem_bytes));
+  lay.off_kpack = off;  off = align256(off + int64_t(heads) * p->rows_per_head * head_dim * int64_t(p->elem_bytes));
+  lay.off_vpack = off;  off = align256(off + int64_t(heads) * p->rows_per_head * head_dim * int64_t(p->elem_bytes));
+  lay.total_bytes = off;
+
+  IndexGeom& g = p->geom;
+  g.L = p->L; g.P = p->P; g.n_special = n_special; g.grid_w = grid_w;
+  g.s_h = s_h; g.s_w = s_w; g.kw = p->kw; g.kept = p->kept;
+  g.ref_dense = p->ref_dense ? 1 : 0; g.subsampled = p->subsampled ? 1 : 0;
+  return VGGT_ATTN_OK;
+}
+
+}  // namespace vggt
