@@ -1,0 +1,242 @@
+#!/usr/bin/env python3
+"""Throughput of VGGT global attention on one MI355X, through the C ABI of libvggt_attn.so.
+
+A step is one vggt_attn_forward of the workload: the gather/pack stage (index set S, packed K/V
+tiles, per-frame mean K/V) followed by the MFMA attention kernel, on inputs already resident in
+HBM.  Default workload: 800 frames x 1374 tokens (37x37 patches + 5 special), 16 heads, d = 64,
+bf16 in / fp32 out, SGA sigma = 6 (2x3 windows) with frame 0 and the specials dense and the
+diagonal + per-frame mean terms on.
+
+Prints one JSON line.  value = attended queries/s (query tokens, each over all heads, per second
+of step time).  roofline = the attention kernel against the bf16 dense matrix-core peak, its
+duration taken from HIP events on the launch stream.  cpu_baseline = the float64 oracle timed
+on a bounded sample of query rows of the same workload on this host's cores (a reported
+baseline, not a target); the same rows double as a parity check of this run's output.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak (vendor figure)
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
+
+METRIC = "global-attn attended queries/s + TFLOP/s (% bf16 MFMA peak), 800 frames sigma=6"
+
+# name -> (plan/oracle descriptor, human description)
+WORKLOADS = {
+    "sga6-800f": (dict(frames=800, grid_h=37, grid_w=37, heads=16, sigma=6, diag=True, mean=True),
+                  "800 frames x 1374 tokens (37x37 patches + 5 special), 16 heads, d=64, bf16 in / fp32 out, "
+                  "SGA sigma=6 (2x3), frame 0 + specials dense, diagonal + per-frame mean K/V (unit weight)"),
+    "dense-32f": (dict(frames=32, grid_h=37, grid_w=37, heads=16, sigma=1),
+                  "32 frames x 1374 tokens, 16 heads, d=64, bf16 in / fp32 out, dense global attention"),
+    "sga4-100f": (dict(frames=100, grid_h=37, grid_w=37, heads=16, sigma=4, diag=True, mean=True),
+                  "100 frames x 1374 tokens, 16 heads, d=64, bf16 in / fp32 out, SGA sigma=4 (2x2), diag + mean"),
+    "g2f-200f": (dict(frames=200, grid_h=37, grid_w=37, heads=16, g2f=True),
+                 "200 frames x 1374 tokens, 16 heads, d=64, bf16 in / fp32 out, Global-to-Frame (3200 batches of 1374x1374)"),
+    "sga9-200f": (dict(frames=200, grid_h=37, grid_w=37, heads=16, sigma=9, diag=True, mean=True),
+                  "200 frames x 1374 tokens, 16 heads, d=64, bf16 in / fp32 out, SGA sigma=9 (3x3), diag + mean"),
+}
+
+KERNEL_SOURCES = ("vggt_global_attention_attn_amd/csrc/attn.hip", "vggt_global_attention_attn_amd/csrc/device_common.h")
+TRAFFIC_FILE = "profiles/attn_{workload}_hbm_traffic.txt"
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per attention launch from the committed rocprofv3 PMC summary, if it was taken
+    on the current kernel source; else None."""
+    path = os.path.join(ROOT, TRAFFIC_FILE.format(workload=workload))
+    if not os.path.exists(path):
+        return None
+    rec = None
+    with open(path) as fh:
+        for line in fh:
+            line = line.strip()
+            if line.startswith("{") and '"source_sha256"' in line:
+                rec = json.loads(line)
+    if not rec or rec.get("source_sha256") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def gather_bytes(desc, c) -> int:
+    """Algorithmic bytes of the gather/pack stage (bf16): read the K/V rows of S and the dropped
+    rows that feed the means, write the packed K/V rows (padding included) and S."""
+    H, d, e = desc["heads"], 64, 2
+    L = 5 + desc["grid_h"] * desc["grid_w"]
+    T = desc["frames"] * L
+    if desc.get("g2f"):
+        rows_read = T
+        rows_written = desc["frames"] * ((L + 63) // 64) * 64
+        index = 0
+    else:
+        n_drop_read = c["n_mean"] and (T - c["n_kv"])  # every dropped token feeds a mean
+        rows_read = c["n_kv"] + (n_drop_read or 0)
+        rows_written = (c["n_kv"] + c["n_mean"] + 63) // 64 * 64
+        index = 4 * c["n_kv"]
+    return int(H * (rows_read + rows_written) * d * e * 2 + index)
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="sga6-800f", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=256, help="query rows in the oracle sample")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="also run one plain device copy of this many MiB (PMC scale calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this library has no multi-GPU path (run with --gpus 1)",
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import vggt_global_attention_attn_amd as va
+    from synth import host_threads, make_qkv, sample_rows
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    desc, description = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    plan = va.Plan(**desc, in_dtype="bf16", out_dtype="fp32")
+    counts = plan.counts()
+    T, H = plan.T, plan.heads
+
+    log(f"workload {args.workload}: T={T} heads={H} |S|={counts['n_kv']} M={counts['n_mean']} "
+        f"n_diag={counts['n_diag']} flops={counts['flops']:.4e}")
+    t0 = time.time()
+    q, k, v = make_qkv(desc["frames"], desc["grid_h"], desc["grid_w"], 5, H, 64, "bf16", seed=0)
+    log(f"inputs drawn in {time.time() - t0:.1f} s")
+
+    def up(x):
+        return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    qd, kd, vd = up(q), up(k), up(v)
+    if args.no_cpu_baseline:
+        del q, k, v
+    out = plan.new_output(dev)
+    ws = plan.new_workspace(dev)
+    torch.cuda.synchronize()
+
+    if args.calib_copy_mib:
+        src = torch.empty(args.calib_copy_mib << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        log(f"calibration copy of {args.calib_copy_mib} MiB done")
+
+    for i in range(args.warmup):
+        plan.forward(qd, kd, vd, out, ws)
+        torch.cuda.synchronize()
+        log(f"warmup {i + 1}/{args.warmup}")
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    for e0, e1, e2 in ev:
+        e0.record()
+        plan.pack(kd, vd, ws)
+        e1.record()
+        plan.attend(qd, kd, vd, out, ws)
+        e2.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    t_gather = sum(e0.elapsed_time(e1) for e0, e1, _ in ev) / len(ev) * 1e-3
+    t_attn = sum(e1.elapsed_time(e2) for _, e1, e2 in ev) / len(ev) * 1e-3
+    step_s = wall / args.steps
+    log(f"timed {args.steps} steps: {step_s * 1e3:.3f} ms/step (gather {t_gather * 1e3:.3f} ms, attention {t_attn * 1e3:.3f} ms)")
+
+    flops = counts["flops"]
+    achieved = flops / t_attn / 1e12
+    traffic = measured_traffic(args.workload)
+    gbytes = gather_bytes(desc, counts)
+    result = {
+        "metric": METRIC,
+        "value": T / step_s,
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": step_s * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": description, "name": args.workload, "frames": desc["frames"], "tokens": T,
+                   "heads": H, "head_dim": 64, "sigma": desc.get("sigma", 1), "kv_tokens": counts["n_kv"],
+                   "mean_tokens": counts["n_mean"], "diag_queries": counts["n_diag"]},
+        "query_heads_per_s": H * T / step_s,
+        "tflops": flops / step_s / 1e12,
+        "pct_bf16_peak": 100.0 * flops / step_s / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+        "t_gather_ms": t_gather * 1e3,
+        "t_attn_ms": t_attn * 1e3,
+        "gather": {"bytes": gbytes, "GB/s": gbytes / t_gather / 1e9, "frac_hbm_peak": gbytes / t_gather / 1e9 / HBM_PEAK_GBS},
+        "roofline": {"bound": "mfma", "kernel": "attn_bf16_kernel", "achieved": achieved,
+                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
+                     "traffic": traffic, "algorithmic_flops_per_launch": flops},
+        "device": torch.cuda.get_device_name(dev),
+    }
+
+    if not args.no_cpu_baseline:
+        import oracle
+        from oracle import Desc
+        rows_all = sample_rows(desc["frames"], desc["grid_h"], desc["grid_w"], 5, count=4096, seed=1)
+        rows = rows_all[:: max(1, rows_all.size // args.cpu_rows)][: args.cpu_rows]
+        odesc = Desc(**desc)
+        cores = host_threads()
+        log(f"oracle on {rows.size} rows x {H} heads with {cores} threads")
+        c0 = time.perf_counter()
+        ref = oracle.attention(q, k, v, odesc, rows=rows, workers=cores)
+        c_s = time.perf_counter() - c0
+        got = out[:, torch.from_numpy(rows).to(dev)].double().cpu().numpy()
+        diff = got - ref
+        result["cpu_baseline"] = {
+            "value": rows.size / c_s, "unit": "queries/s", "cores": cores, "kind": "oracle",
+            "sample": f"{rows.size} seeded query rows (all {H} heads) of the same workload, float64 NumPy, "
+                      f"{c_s:.1f} s including its own index-set and mean computation",
+            "seconds": c_s,
+        }
+        result["parity_sample"] = {"rows": int(rows.size), "max_abs": float(np.abs(diff).max()),
+                                   "rel_l2": float(np.linalg.norm(diff) / np.linalg.norm(ref))}
+        log(f"oracle {c_s:.1f} s; parity max-abs {result['parity_sample']['max_abs']:.3e} "
+            f"rel-L2 {result['parity_sample']['rel_l2']:.3e}")
+
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

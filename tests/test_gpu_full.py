@@ -1,0 +1,68 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration the benchmark times
+(pack + attend through the C ABI), on 4096 seeded query rows per workload (all heads), which
+the oracle computes one by one; plus the bit-exact index set and |D_f| at full size.
+
+Workloads: dense 32 frames; SGA sigma 4 at 100 frames (UNIT and COUNT means); G2F and SGA
+sigma 9 on the same 200-frame tensors; SGA sigma 6 at 800 frames.  All use 37x37 patches + 5
+special tokens per frame, 16 heads, d = 64, bf16 inputs and fp32 output."""
+import numpy as np
+import pytest
+
+import oracle
+from oracle import Desc
+from synth import host_threads, make_qkv, sample_rows
+from tests.gpu_util import assert_close, errors, plan_kwargs
+
+pytestmark = pytest.mark.gpu
+
+FULL = [
+    ("dense-32f", Desc(32, 37, 37, 16, sigma=1)),
+    ("sga4-100f", Desc(100, 37, 37, 16, sigma=4, diag=True, mean=True)),
+    ("sga4-100f-count", Desc(100, 37, 37, 16, sigma=4, diag=True, mean=True, mean_count=True)),
+    ("g2f-200f", Desc(200, 37, 37, 16, g2f=True)),
+    ("sga9-200f", Desc(200, 37, 37, 16, sigma=9, diag=True, mean=True)),
+    ("sga6-800f", Desc(800, 37, 37, 16, sigma=6, diag=True, mean=True)),
+]
+
+_cache = {}
+
+
+def device_inputs(desc):
+    """Host and device copies of the seeded inputs of a geometry (one geometry cached)."""
+    import torch
+    key = (desc.frames, desc.grid_h, desc.grid_w, desc.heads)
+    if key not in _cache:
+        _cache.clear()
+        q, k, v = make_qkv(desc.frames, desc.grid_h, desc.grid_w, desc.n_special, desc.heads, desc.head_dim,
+                           "bf16", seed=0)
+        up = lambda x: torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda()
+        _cache[key] = ((q, k, v), (up(q), up(k), up(v)))
+    return _cache[key]
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name,desc", FULL, ids=[n for n, _ in FULL])
+def test_full_size_sampled_rows(name, desc):
+    import torch
+    import vggt_global_attention_attn_amd as va
+    print(f"[full] {name}: drawing inputs", flush=True)
+    (q, k, v), (qd, kd, vd) = device_inputs(desc)
+    plan = va.Plan(**plan_kwargs(desc))
+    out = plan.new_output()
+    ws = plan.new_workspace()
+    print(f"[full] {name}: pack + attend", flush=True)
+    plan.pack(kd, vd, ws)
+    plan.attend(qd, kd, vd, out, ws)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(out).all())
+    if not desc.g2f:
+        idx, dcount = plan.index_set(ws)
+        assert np.array_equal(idx, oracle.index_set(desc))
+        assert np.array_equal(dcount, oracle.dropped_counts(desc).astype(np.int32))
+    rows = sample_rows(desc.frames, desc.grid_h, desc.grid_w, desc.n_special, count=4096, seed=1)
+    got = out[:, torch.from_numpy(rows).cuda()].double().cpu().numpy()
+    del out, ws
+    print(f"[full] {name}: oracle on {rows.size} rows", flush=True)
+    ref = oracle.attention(q, k, v, desc, rows=rows, workers=host_threads())
+    print(f"[full] {name}: max-abs %.3e rel-L2 %.3e" % errors(got, ref), flush=True)
+    assert_close(got, ref, fp32=False, label=name)

@@ -31,7 +31,7 @@ def hipcc() -> str:
 
 def commands(out: str = LIB, extra: list[str] | None = None) -> list[list[str]]:
     extra = extra or []
-    objdir = os.path.join(ROOT, "_build")
+    objdir = os.path.join(ROOT, "_build", os.path.basename(out))
     os.makedirs(objdir, exist_ok=True)
     cmds, objs = [], []
     common = ["-O3", "-std=c++17", "-fPIC", "-I", INCLUDE, "-I", CSRC, "-Wall", "-Wno-unused-function"]
@@ -49,9 +49,10 @@ def commands(out: str = LIB, extra: list[str] | None = None) -> list[list[str]]:
     return cmds
 
 
-def build(verbose: bool = False, out: str = LIB) -> str:
-    """Compile every source and link the shared library; returns its path."""
-    for cmd in commands(out):
+def build(verbose: bool = False, out: str = LIB, extra: list[str] | None = None) -> str:
+    """Compile every source and link the shared library; returns its path.  `extra` adds
+    compiler flags (e.g. -D tile-shape macros of attn.hip)."""
+    for cmd in commands(out, extra):
         if verbose:
             print(" ".join(shlex.quote(c) for c in cmd), flush=True)
         res = subprocess.run(cmd, capture_output=True, text=True)

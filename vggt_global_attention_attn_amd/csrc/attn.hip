@@ -20,12 +20,30 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <type_traits>
 
 #include "device_common.h"
 #include "launch.h"
 
+#ifndef VGGT_GLOBAL_QB
+#define VGGT_GLOBAL_QB 2
+#endif
+#ifndef VGGT_GLOBAL_WPE
+#define VGGT_GLOBAL_WPE 3
+#endif
+#ifndef VGGT_G2F_QB
+#define VGGT_G2F_QB 2
+#endif
+#ifndef VGGT_G2F_WPE
+#define VGGT_G2F_WPE 2
+#endif
+
 namespace vggt {
 namespace {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+constexpr float kLazyRescale = 8.f;  // log2 units
+constexpr bf16x2_t kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
 
 struct AttnArgs {
   const void* q;
@@ -41,7 +59,8 @@ struct AttnArgs {
   int n_plain;     // keys before the mean keys
   int nktiles;     // ceil(nkeys / 64)
   int slow_from;   // first tile that holds a mean key or padding
-  float bias_s;    // added to the raw score q.k of a mean key (COUNT weighting), else 0
+  float bias_s;    // fp32 path: added to the raw score q.k of a mean key (COUNT), else 0
+  float bias_log2; // bf16 path: the same bias in log2 units, ln|D_f| * log2(e)
   float c_log2;    // tau * log2(e)
   int qtiles;      // query tiles per head
   int g2f;
@@ -50,26 +69,46 @@ struct AttnArgs {
   IndexGeom g;
 };
 
-__device__ __forceinline__ float wave_max_across_groups(float x) {
-  // Lanes l, l^16, l^32, l^48 hold the same query; combine them.
-  x = fmaxf(x, __shfl_xor(x, 16));
-  x = fmaxf(x, __shfl_xor(x, 32));
-  return x;
+// Plain v_max_f32 / v_max3_f32: scores are never NaN, and fmaxf would add canonicalising
+// moves and does not fuse into max3 on its own.
+__device__ __forceinline__ float vmax(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+__device__ __forceinline__ float max3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
 }
 
-__device__ __forceinline__ float wave_sum_across_groups(float x) {
-  x += __shfl_xor(x, 16);
-  x += __shfl_xor(x, 32);
-  return x;
+// Lanes l, l^16, l^32 and l^48 hold the same query.  v_permlane16_swap(x, x) leaves each
+// lane holding its own value and its xor-16 partner's in the two results; v_permlane32_swap
+// does the same for the xor-32 partner.  Pure VALU, no LDS round trip.
+__device__ __forceinline__ float group_max(float x) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = vmax(__uint_as_float(p[0]), __uint_as_float(p[1]));
+  const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return vmax(__uint_as_float(q[0]), __uint_as_float(q[1]));
+}
+__device__ __forceinline__ float group_sum(float x) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+  const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(q[0]) + __uint_as_float(q[1]);
 }
 
-template <int QB, bool OUT_BF16>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+template <int QB, int WPE, bool OUT_BF16>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 void attn_bf16_kernel(AttnArgs a) {
   constexpr int WQ = 16 * QB;  // query rows per wave
   constexpr int BM = 4 * WQ;   // query rows per work-group
-  // [buffer][0 = K tile, 1 = V tile][64 rows x 128 bytes], 16-byte chunks XOR-swizzled by row.
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2][2][kTile * 128];
+  // Two K tiles and two V tiles of 64 rows x 128 bytes; 16-byte chunks XOR-swizzled by row so
+  // that the 16-byte operand reads of 8 consecutive lanes hit distinct banks.  The K stream runs
+  // one tile ahead of the V stream: step j reads K tile j+1 (scores of the next tile) and V tile
+  // j (output of the current tile).
+  __shared__ __attribute__((aligned(16))) uint8_t kbuf[2][kTile * 128];
+  __shared__ __attribute__((aligned(16))) uint8_t vbuf[2][kTile * 128];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, grp = lane >> 4;
@@ -96,43 +135,42 @@ void attn_bf16_kernel(AttnArgs a) {
   const uint16_t* vseg = static_cast<const uint16_t*>(a.vpack) + seg_off;
 
   // Q as the B operand of S^T = K Q^T: lane (l16, grp) holds query l16 of its block and
-  // channels c*32 + grp*8 .. +7 for c = 0, 1.
+  // channels cc*32 + grp*8 .. +7 for cc = 0, 1.  Q is scaled once by c = tau*log2(e) and
+  // rounded back to bf16, so the matrix core yields scores directly in log2 units and the
+  // softmax exponent needs no per-score multiply.
   bf16x8_t qf[QB][2];
-  float m_run[QB], l_run[QB];
+  float m_run[QB], l_run[QB];  // running max (log2 units) and lane-partial row sum
   f32x4_t o[QB][4];
   const float c = a.c_log2;
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int64_t t = wrow0 + qb * 16 + l16;
     const bool valid = t < row_end;
-#pragma unroll
-    for (int cc = 0; cc < 2; ++cc) {
-      uint4 raw = make_uint4(0, 0, 0, 0);
-      if (valid) raw = *reinterpret_cast<const uint4*>(Q + size_t(t) * kHeadDim + cc * 32 + grp * 8);
-      qf[qb][cc] = __builtin_bit_cast(bf16x8_t, raw);
-    }
-    // Diagonal prologue: a query whose own token is not in S starts with its self term,
-    // m = tau*log2(e)*q.k_self, l = 1, O = v_self.
-    const bool self = a.diag && valid && !token_kept(a.g, t);
     float dot = 0.f;
-    uint4 kr[2] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0)};
-    if (self) {
-      kr[0] = *reinterpret_cast<const uint4*>(Kin + size_t(t) * kHeadDim + grp * 8);
-      kr[1] = *reinterpret_cast<const uint4*>(Kin + size_t(t) * kHeadDim + 32 + grp * 8);
-    }
+    const bool self = a.diag && valid && !token_kept(a.g, t);
 #pragma unroll
     for (int cc = 0; cc < 2; ++cc) {
-      const uint4 qraw = __builtin_bit_cast(uint4, qf[qb][cc]);
-      const uint32_t qw[4] = {qraw.x, qraw.y, qraw.z, qraw.w};
-      const uint32_t kw[4] = {kr[cc].x, kr[cc].y, kr[cc].z, kr[cc].w};
+      uint4 raw = make_uint4(0, 0, 0, 0), kraw = make_uint4(0, 0, 0, 0);
+      if (valid) raw = *reinterpret_cast<const uint4*>(Q + size_t(t) * kHeadDim + cc * 32 + grp * 8);
+      if (self) kraw = *reinterpret_cast<const uint4*>(Kin + size_t(t) * kHeadDim + cc * 32 + grp * 8);
+      const uint32_t qw[4] = {raw.x, raw.y, raw.z, raw.w};
+      const uint32_t kw[4] = {kraw.x, kraw.y, kraw.z, kraw.w};
+      bf16x8_t v;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        dot = fmaf(__uint_as_float(qw[i] << 16), __uint_as_float(kw[i] << 16), dot);
-        dot = fmaf(__uint_as_float(qw[i] & 0xffff0000u), __uint_as_float(kw[i] & 0xffff0000u), dot);
+        const float q0 = __uint_as_float(qw[i] << 16) * c, q1 = __uint_as_float(qw[i] & 0xffff0000u) * c;
+        v[2 * i] = (__bf16)q0;
+        v[2 * i + 1] = (__bf16)q1;
+        // Diagonal self logit from the same scaled query the matrix core uses.
+        dot = fmaf(float(v[2 * i]), __uint_as_float(kw[i] << 16), dot);
+        dot = fmaf(float(v[2 * i + 1]), __uint_as_float(kw[i] & 0xffff0000u), dot);
       }
+      qf[qb][cc] = v;
     }
-    dot = wave_sum_across_groups(dot);
-    m_run[qb] = self ? dot * c : -INFINITY;
+    // Diagonal term: a query whose own token is not in S starts with its self term
+    // (m = self logit, l = 1, O = v_self); the others start empty.
+    dot = group_sum(dot);
+    m_run[qb] = self ? dot : -INFINITY;
     l_run[qb] = (self && grp == 0) ? 1.f : 0.f;
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
@@ -148,127 +186,207 @@ void attn_bf16_kernel(AttnArgs a) {
     }
   }
 
-  // Global -> LDS staging of one tile: 512 chunks of 16 bytes per tensor, 2 per thread.
-  auto load_tile = [&](int j, uint4 (&kr)[2], uint4 (&vr)[2]) {
-    const uint16_t* kt = kseg + size_t(j) * kTile * kHeadDim;
-    const uint16_t* vt = vseg + size_t(j) * kTile * kHeadDim;
+  // Global -> LDS staging of one tile of one tensor: 512 chunks of 16 bytes, 2 per thread.
+  auto load_tile = [&](const uint16_t* base, int j, uint4 (&r)[2]) {
+    const uint16_t* t = base + size_t(j) * kTile * kHeadDim;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int e = tid + 256 * i;
-      kr[i] = *reinterpret_cast<const uint4*>(kt + e * 8);
-      vr[i] = *reinterpret_cast<const uint4*>(vt + e * 8);
-    }
+    for (int i = 0; i < 2; ++i) r[i] = *reinterpret_cast<const uint4*>(t + (tid + 256 * i) * 8);
   };
-  auto store_tile = [&](int b, const uint4 (&kr)[2], const uint4 (&vr)[2]) {
+  auto store_tile = [&](uint8_t* buf, const uint4 (&r)[2]) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int e = tid + 256 * i;
       const int row = e >> 3, ch = e & 7;
-      const int off = row * 128 + ((ch ^ (row & 7)) << 4);
-      *reinterpret_cast<uint4*>(&smem[b][0][off]) = kr[i];
-      *reinterpret_cast<uint4*>(&smem[b][1][off]) = vr[i];
+      *reinterpret_cast<uint4*>(&buf[row * 128 + ((ch ^ (row & 7)) << 4)]) = r[i];
     }
   };
+  // 16-byte operand read of LDS row `row`, chunk `ch` (undoing the swizzle).
+  auto lds_frag = [&](const uint8_t* buf, int row, int ch) {
+    return *reinterpret_cast<const bf16x8_t*>(&buf[row * 128 + ((ch ^ (row & 7)) << 4)]);
+  };
 
-  const int nkt = a.nktiles;
-  {
-    uint4 kr[2], vr[2];
-    load_tile(0, kr, vr);
-    store_tile(0, kr, vr);
-  }
-  __syncthreads();
-
-  for (int j = 0; j < nkt; ++j) {
-    const int b = j & 1;
-    uint4 kr[2], vr[2];
-    const bool more = j + 1 < nkt;
-    if (more) load_tile(j + 1, kr, vr);
-
-    // ---- S^T = K Q^T for 64 keys x WQ queries ----
-    f32x4_t s[QB][4];
+  // S'^T = K Q'^T - m for 64 keys x WQ queries: the running max enters as the accumulator's
+  // initial value, so the scores leave the matrix core already shifted (log2 units).
+  auto scores = [&](const uint8_t* kb, f32x4_t (&s)[QB][4]) {
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      const int row = kb * 16 + l16;
-      const bf16x8_t k0 = *reinterpret_cast<const bf16x8_t*>(&smem[b][0][row * 128 + (((0 + grp) ^ (row & 7)) << 4)]);
-      const bf16x8_t k1 = *reinterpret_cast<const bf16x8_t*>(&smem[b][0][row * 128 + (((4 + grp) ^ (row & 7)) << 4)]);
+    for (int k4 = 0; k4 < 4; ++k4) {
+      const int row = k4 * 16 + l16;
+      const bf16x8_t k0 = lds_frag(kb, row, grp), k1 = lds_frag(kb, row, 4 + grp);
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+        const float mneg = -m_run[qb];
+        f32x4_t acc = {mneg, mneg, mneg, mneg};
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[qb][0], acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qf[qb][1], acc, 0, 0, 0);
-        s[qb][kb] = acc;
+        s[qb][k4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qf[qb][1], acc, 0, 0, 0);
       }
     }
-
-    // ---- mean-key bias and padding mask (only the last few tiles) ----
-    if (j >= a.slow_from) {
+  };
+  // Mean-key bias and padding mask, only for the last tiles of the segment.
+  auto bias_mask = [&](int j, f32x4_t (&s)[QB][4]) {
+    if (j < a.slow_from) return;
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
+    for (int k4 = 0; k4 < 4; ++k4) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = j * kTile + kb * 16 + grp * 4 + i;
-          const float add = key >= a.nkeys ? -INFINITY : (key >= a.n_plain ? a.bias_s : 0.f);
+      for (int i = 0; i < 4; ++i) {
+        const int key = j * kTile + k4 * 16 + grp * 4 + i;
+        const float add = key >= a.nkeys ? -INFINITY : (key >= a.n_plain ? a.bias_log2 : 0.f);
 #pragma unroll
-          for (int qb = 0; qb < QB; ++qb) s[qb][kb][i] += add;
-        }
+        for (int qb = 0; qb < QB; ++qb) s[qb][k4][i] += add;
       }
     }
-
-    // ---- online softmax ----
-    bf16x8_t pf[QB][2];
+  };
+  auto row_max = [&](const f32x4_t (&s)[4]) {
+    float mx = max3(s[0][0], s[0][1], s[0][2]);
+    mx = max3(mx, s[0][3], s[1][0]);
+    mx = max3(mx, s[1][1], s[1][2]);
+    mx = max3(mx, s[1][3], s[2][0]);
+    mx = max3(mx, s[2][1], s[2][2]);
+    mx = max3(mx, s[2][3], s[3][0]);
+    mx = max3(mx, s[3][1], s[3][2]);
+    return group_max(vmax(mx, s[3][3]));
+  };
+  // Raise the running max by d >= 0 (scores of the tile in hand are relative to the old m).
+  auto raise_max = [&](int qb, float d, f32x4_t (&s)[4]) {
+    asm volatile("; rare rescale" ::);  // keeps this branch from being speculated into every tile
+    const float alpha = __builtin_amdgcn_exp2f(-d);
+    m_run[qb] += d;
+    l_run[qb] *= alpha;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      o[qb][k] *= alpha;
+      s[k] -= d;
+    }
+  };
+  // Lazy rescale: m is only raised when a tile's (shifted) max exceeds 2^8.  Until then
+  // p = 2^s' <= 2^8, exact in bf16's range and in the float32 sums, and the O/l rescale (the
+  // costliest VALU step) is skipped; O/l is the same quotient either way.
+  auto update_max = [&](f32x4_t (&s)[QB][4]) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      float mx = s[qb][0][0];
+      const float mx = row_max(s[qb]);
+      if (__builtin_amdgcn_ballot_w64(mx > kLazyRescale) != 0) raise_max(qb, vmax(mx, 0.f), s[qb]);
+    }
+  };
+  // p = 2^s' rounded to bf16, already in the B-operand layout of the PV product; the row sum
+  // uses the same rounded weights.
+  auto probabilities = [&](const f32x4_t (&s)[QB][4], bf16x8_t (&pf)[QB][2]) {
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[qb][kb][i]);
-      mx = wave_max_across_groups(mx);
-      const float m_new = fmaxf(m_run[qb], mx * c);
-      const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - m_new);
-      m_run[qb] = m_new;
-      float lsum = 0.f;
-      float p[4][4];
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          p[kb][i] = __builtin_amdgcn_exp2f(fmaf(s[qb][kb][i], c, -m_new));
-          lsum += p[kb][i];
-        }
-      l_run[qb] = l_run[qb] * alpha + lsum;
-#pragma unroll
-      for (int db = 0; db < 4; ++db) o[qb][db] *= alpha;
+    for (int qb = 0; qb < QB; ++qb) {
+      float l = l_run[qb];
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) {
-        const uint4 w = make_uint4(pack_bf16x2(p[2 * h2][0], p[2 * h2][1]), pack_bf16x2(p[2 * h2][2], p[2 * h2][3]),
-                                   pack_bf16x2(p[2 * h2 + 1][0], p[2 * h2 + 1][1]),
-                                   pack_bf16x2(p[2 * h2 + 1][2], p[2 * h2 + 1][3]));
-        pf[qb][h2] = __builtin_bit_cast(bf16x8_t, w);
+        const f32x4_t& s0 = s[qb][2 * h2];
+        const f32x4_t& s1 = s[qb][2 * h2 + 1];
+        const bf16x8_t pv = {
+            (__bf16)__builtin_amdgcn_exp2f(s0[0]), (__bf16)__builtin_amdgcn_exp2f(s0[1]),
+            (__bf16)__builtin_amdgcn_exp2f(s0[2]), (__bf16)__builtin_amdgcn_exp2f(s0[3]),
+            (__bf16)__builtin_amdgcn_exp2f(s1[0]), (__bf16)__builtin_amdgcn_exp2f(s1[1]),
+            (__bf16)__builtin_amdgcn_exp2f(s1[2]), (__bf16)__builtin_amdgcn_exp2f(s1[3])};
+        pf[qb][h2] = pv;
+        l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pv, pv, 0, 1), kOnes2, l, false);
+        l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pv, pv, 2, 3), kOnes2, l, false);
+        l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pv, pv, 4, 5), kOnes2, l, false);
+        l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pv, pv, 6, 7), kOnes2, l, false);
       }
+      l_run[qb] = l;
     }
-
-    // ---- O^T += V^T P^T ----
+  };
+  // O^T += V^T P^T.
+  auto accumulate = [&](const uint8_t* vb, const bf16x8_t (&pf)[QB][2]) {
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
       const int row = db * 16 + l16;
-      const bf16x8_t v0 = *reinterpret_cast<const bf16x8_t*>(&smem[b][1][row * 128 + (((0 + grp) ^ (row & 7)) << 4)]);
-      const bf16x8_t v1 = *reinterpret_cast<const bf16x8_t*>(&smem[b][1][row * 128 + (((4 + grp) ^ (row & 7)) << 4)]);
+      const bf16x8_t v0 = lds_frag(vb, row, grp), v1 = lds_frag(vb, row, 4 + grp);
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
         o[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v0, pf[qb][0], o[qb][db], 0, 0, 0);
         o[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v1, pf[qb][1], o[qb][db], 0, 0, 0);
       }
     }
+  };
 
-    if (more) store_tile(b ^ 1, kr, vr);
+  const int nkt = a.nktiles;
+  {
+    uint4 r[2];
+    load_tile(kseg, 0, r);
+    store_tile(kbuf[0], r);
+    load_tile(vseg, 0, r);
+    store_tile(vbuf[0], r);
+    if (nkt > 1) {
+      load_tile(kseg, 1, r);
+      store_tile(kbuf[1], r);
+    }
+  }
+  __syncthreads();
+
+  // One pipelined step: finish tile j (scores s_cur) while the scores of tile j+1 are formed.
+  // MASK = tile j+1 may hold mean keys or padding (kept out of the steady-state loop, where the
+  // compiler would otherwise if-convert the bias into every tile).
+  auto step = [&](auto mask_tag, int j, f32x4_t (&s_cur)[QB][4], f32x4_t (&s_next)[QB][4]) {
+    uint4 kr[2], vr[2];
+    load_tile(kseg, min(j + 2, nkt - 1), kr);
+    load_tile(vseg, j + 1, vr);
+    update_max(s_cur);
+    scores(kbuf[(j + 1) & 1], s_next);
+    bf16x8_t pf[QB][2];
+    probabilities(s_cur, pf);
+    accumulate(vbuf[j & 1], pf);
+    store_tile(kbuf[j & 1], kr);
+    store_tile(vbuf[(j + 1) & 1], vr);
+    if constexpr (decltype(mask_tag)::value) bias_mask(j + 1, s_next);
     __syncthreads();
+  };
+  auto last = [&](int j, f32x4_t (&s_cur)[QB][4]) {
+    update_max(s_cur);
+    bf16x8_t pf[QB][2];
+    probabilities(s_cur, pf);
+    accumulate(vbuf[j & 1], pf);
+  };
+  using plain_t = std::integral_constant<bool, false>;
+  using masked_t = std::integral_constant<bool, true>;
+
+  // Tile 0 sets the running max exactly (from the diagonal term, if any, and the tile).
+  f32x4_t sa[QB][4], sb[QB][4];
+  float m0[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    m0[qb] = m_run[qb];
+    m_run[qb] = 0.f;
+  }
+  scores(kbuf[0], sa);
+  bias_mask(0, sa);
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const float m_new = vmax(m0[qb], row_max(sa[qb]));  // finite: tile 0 holds a valid key
+    const float alpha = __builtin_amdgcn_exp2f(m0[qb] - m_new);
+    m_run[qb] = m_new;
+    l_run[qb] *= alpha;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      o[qb][k] *= alpha;
+      sa[qb][k] -= m_new;
+    }
+  }
+  int j = 0;
+  for (; j + 2 < nkt && j + 2 < a.slow_from; j += 2) {
+    step(plain_t{}, j, sa, sb);
+    step(plain_t{}, j + 1, sb, sa);
+  }
+  for (; j + 2 < nkt; j += 2) {
+    step(masked_t{}, j, sa, sb);
+    step(masked_t{}, j + 1, sb, sa);
+  }
+  if (j + 1 < nkt) {
+    step(masked_t{}, j, sa, sb);
+    last(j + 1, sb);
+  } else {
+    last(j, sa);
   }
 
   // ---- epilogue: O / l ----
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    const float l = wave_sum_across_groups(l_run[qb]);
+    const float l = group_sum(l_run[qb]);
     const float inv = 1.f / l;
     const int64_t t = wrow0 + qb * 16 + l16;
     if (t >= row_end) continue;
@@ -398,6 +516,7 @@ hipError_t launch_attend(const vggt_attn_plan_s& p, const void* q, const void* k
   // COUNT: logit += ln|D_f|  <=>  raw score q.k += ln|D_f| / tau.
   a.bias_s = (p.mean_count && p.M > 0) ? float(std::log(double(p.dropped)) / tau) : 0.f;
   a.c_log2 = float(tau * 1.4426950408889634);
+  a.bias_log2 = (p.mean_count && p.M > 0) ? float(std::log2(double(p.dropped))) : 0.f;
   a.g2f = p.g2f ? 1 : 0;
   a.diag = p.diag ? 1 : 0;
   a.g = p.geom;
@@ -415,10 +534,12 @@ hipError_t launch_attend(const vggt_attn_plan_s& p, const void* q, const void* k
     return hipGetLastError();
   }
 
-  // bf16: 64 queries per wave for the global forms (K/V traffic halves against 32), 32 per
-  // wave under G2F (1374-token frames pad to 1408 instead of 1536 query rows).
-  const bool small = p.g2f;
-  const int BM = small ? 128 : 256;
+  // bf16: QB blocks of 16 query rows per wave, 4 waves per work-group, WPE work-groups'
+  // waves per SIMD (occupancy), so that the matrix-core phase of one work-group overlaps the
+  // softmax phase of another on the same CU.
+  constexpr int QBg = VGGT_GLOBAL_QB, WPEg = VGGT_GLOBAL_WPE;
+  constexpr int QBf = VGGT_G2F_QB, WPEf = VGGT_G2F_WPE;
+  const int BM = 64 * (p.g2f ? QBf : QBg);
   if (p.g2f) {
     a.qtiles_per_frame = int((p.L + BM - 1) / BM);
     a.qtiles = a.qtiles_per_frame * p.frames;
@@ -427,12 +548,12 @@ hipError_t launch_attend(const vggt_attn_plan_s& p, const void* q, const void* k
   }
   const unsigned blocks = unsigned(int64_t(a.qtiles) * p.heads);
   const bool ob = p.out_dtype == VGGT_ATTN_BF16;
-  if (small) {
-    if (ob) hipLaunchKernelGGL((attn_bf16_kernel<2, true>), dim3(blocks), dim3(256), 0, stream, a);
-    else hipLaunchKernelGGL((attn_bf16_kernel<2, false>), dim3(blocks), dim3(256), 0, stream, a);
+  if (p.g2f) {
+    if (ob) hipLaunchKernelGGL((attn_bf16_kernel<QBf, WPEf, true>), dim3(blocks), dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL((attn_bf16_kernel<QBf, WPEf, false>), dim3(blocks), dim3(256), 0, stream, a);
   } else {
-    if (ob) hipLaunchKernelGGL((attn_bf16_kernel<4, true>), dim3(blocks), dim3(256), 0, stream, a);
-    else hipLaunchKernelGGL((attn_bf16_kernel<4, false>), dim3(blocks), dim3(256), 0, stream, a);
+    if (ob) hipLaunchKernelGGL((attn_bf16_kernel<QBg, WPEg, true>), dim3(blocks), dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL((attn_bf16_kernel<QBg, WPEg, false>), dim3(blocks), dim3(256), 0, stream, a);
   }
   return hipGetLastError();
 }
