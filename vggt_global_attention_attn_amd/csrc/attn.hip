@@ -10,7 +10,7 @@
 //
 // attn_bf16_kernel: flash-style forward on the bf16 matrix cores (v_mfma_f32_16x16x32_bf16,
 // float32 accumulation).  A work-group of 4 waves owns BM = 4*16*QB query rows of one head and
-// streams the key segment in 64-key tiles through double-buffered LDS.  Scores are formed
+// streams the key segment in 64-key tiles through LDS filled by direct global->LDS copies.  Scores are formed
 // transposed, S^T = K Q^T, so each lane holds 4 keys x 1 query per 16x16 block: the row max
 // is a 16-value in-lane max plus two cross-lane steps, the row sum stays lane-local until the
 // epilogue, and the bf16 probabilities are already laid out as the B operand of
@@ -26,10 +26,10 @@
 #include "launch.h"
 
 #ifndef VGGT_GLOBAL_QB
-#define VGGT_GLOBAL_QB 2
+#define VGGT_GLOBAL_QB 3
 #endif
 #ifndef VGGT_GLOBAL_WPE
-#define VGGT_GLOBAL_WPE 3
+#define VGGT_GLOBAL_WPE 2
 #endif
 #ifndef VGGT_G2F_QB
 #define VGGT_G2F_QB 2
@@ -43,6 +43,8 @@ namespace {
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 constexpr float kLazyRescale = 8.f;  // log2 units
+// s_waitcnt immediate for vmcnt(0) with expcnt and lgkmcnt left at their maxima (gfx9 encoding).
+constexpr int kWaitVmcnt0 = 0x0F70;
 constexpr bf16x2_t kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
 
 struct AttnArgs {
@@ -107,8 +109,14 @@ void attn_bf16_kernel(AttnArgs a) {
   // that the 16-byte operand reads of 8 consecutive lanes hit distinct banks.  The K stream runs
   // one tile ahead of the V stream: step j reads K tile j+1 (scores of the next tile) and V tile
   // j (output of the current tile).
-  __shared__ __attribute__((aligned(16))) uint8_t kbuf[2][kTile * 128];
-  __shared__ __attribute__((aligned(16))) uint8_t vbuf[2][kTile * 128];
+  // Four separate LDS objects (not one array), so that the copy into one buffer is known not
+  // to alias reads of the others and no wait is placed in front of those reads.
+  __shared__ __attribute__((aligned(16))) uint8_t kbuf0[kTile * 128];
+  __shared__ __attribute__((aligned(16))) uint8_t kbuf1[kTile * 128];
+  __shared__ __attribute__((aligned(16))) uint8_t vbuf0[kTile * 128];
+  __shared__ __attribute__((aligned(16))) uint8_t vbuf1[kTile * 128];
+  auto kbuf = [&](auto par) -> uint8_t* { if constexpr (decltype(par)::value == 0) return kbuf0; else return kbuf1; };
+  auto vbuf = [&](auto par) -> uint8_t* { if constexpr (decltype(par)::value == 0) return vbuf0; else return vbuf1; };
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, grp = lane >> 4;
@@ -186,20 +194,23 @@ void attn_bf16_kernel(AttnArgs a) {
     }
   }
 
-  // Global -> LDS staging of one tile of one tensor: 512 chunks of 16 bytes, 2 per thread.
-  auto load_tile = [&](const uint16_t* base, int j, uint4 (&r)[2]) {
-    const uint16_t* t = base + size_t(j) * kTile * kHeadDim;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) r[i] = *reinterpret_cast<const uint4*>(t + (tid + 256 * i) * 8);
-  };
-  auto store_tile = [&](uint8_t* buf, const uint4 (&r)[2]) {
+  // Global -> LDS copy of one 64x128-byte tile with global_load_lds_dwordx4: lane L of a wave
+  // instruction writes the 16 bytes at LDS base + 16*L, so each lane fetches the global chunk
+  // that belongs at that position of the swizzled layout.  8 wave instructions per tile (2 per
+  // wave); no registers are used and completion is awaited (vmcnt) before the step's barrier.
+  auto async_tile = [&](const uint16_t* base, int j, uint8_t* buf) {
+    const uint8_t* t = reinterpret_cast<const uint8_t*>(base + size_t(j) * kTile * kHeadDim);
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const int e = tid + 256 * i;
-      const int row = e >> 3, ch = e & 7;
-      *reinterpret_cast<uint4*>(&buf[row * 128 + ((ch ^ (row & 7)) << 4)]) = r[i];
+      const int blk = i * 4 + wave;              // which 1 KB of the tile this instruction fills
+      const int row = blk * 8 + (lane >> 3);     // 8 rows of 128 bytes per KB
+      const int ch = (lane & 7) ^ (row & 7);     // global chunk that lands at position lane & 7
+      __builtin_amdgcn_global_load_lds(
+          (__attribute__((address_space(1))) void*)(t + row * 128 + ch * 16),
+          (__attribute__((address_space(3))) void*)(buf + blk * 1024), 16, 0, 0);
     }
   };
+  auto wait_tiles = [&]() { __builtin_amdgcn_s_waitcnt(kWaitVmcnt0); };
   // 16-byte operand read of LDS row `row`, chunk `ch` (undoing the swizzle).
   auto lds_frag = [&](const uint8_t* buf, int row, int ch) {
     return *reinterpret_cast<const bf16x8_t*>(&buf[row * 128 + ((ch ^ (row & 7)) << 4)]);
@@ -306,44 +317,41 @@ void attn_bf16_kernel(AttnArgs a) {
   };
 
   const int nkt = a.nktiles;
-  {
-    uint4 r[2];
-    load_tile(kseg, 0, r);
-    store_tile(kbuf[0], r);
-    load_tile(vseg, 0, r);
-    store_tile(vbuf[0], r);
-    if (nkt > 1) {
-      load_tile(kseg, 1, r);
-      store_tile(kbuf[1], r);
-    }
-  }
+  async_tile(kseg, 0, kbuf0);
+  async_tile(vseg, 0, vbuf0);
+  if (nkt > 1) async_tile(kseg, 1, kbuf1);
+  wait_tiles();
   __syncthreads();
 
   // One pipelined step: finish tile j (scores s_cur) while the scores of tile j+1 are formed.
-  // MASK = tile j+1 may hold mean keys or padding (kept out of the steady-state loop, where the
-  // compiler would otherwise if-convert the bias into every tile).
-  auto step = [&](auto mask_tag, int j, f32x4_t (&s_cur)[QB][4], f32x4_t (&s_next)[QB][4]) {
-    uint4 kr[2], vr[2];
-    load_tile(kseg, min(j + 2, nkt - 1), kr);
-    load_tile(vseg, j + 1, vr);
+  // P = j & 1 is a compile-time constant, so every LDS buffer is static.  MASK = tile j+1 may
+  // hold mean keys or padding (kept out of the steady-state loop, where the compiler would
+  // otherwise if-convert the bias into every tile).
+  auto step = [&](auto parity, auto mask_tag, int j, f32x4_t (&s_cur)[QB][4], f32x4_t (&s_next)[QB][4]) {
+    constexpr int P = decltype(parity)::value;
+    using same_t = std::integral_constant<int, P>;
+    using other_t = std::integral_constant<int, P ^ 1>;
+    async_tile(kseg, min(j + 2, nkt - 1), kbuf(same_t{}));
+    async_tile(vseg, j + 1, vbuf(other_t{}));
     update_max(s_cur);
-    scores(kbuf[(j + 1) & 1], s_next);
+    scores(kbuf(other_t{}), s_next);
     bf16x8_t pf[QB][2];
     probabilities(s_cur, pf);
-    accumulate(vbuf[j & 1], pf);
-    store_tile(kbuf[j & 1], kr);
-    store_tile(vbuf[(j + 1) & 1], vr);
+    accumulate(vbuf(same_t{}), pf);
     if constexpr (decltype(mask_tag)::value) bias_mask(j + 1, s_next);
+    wait_tiles();
     __syncthreads();
   };
-  auto last = [&](int j, f32x4_t (&s_cur)[QB][4]) {
+  auto last = [&](auto parity, f32x4_t (&s_cur)[QB][4]) {
     update_max(s_cur);
     bf16x8_t pf[QB][2];
     probabilities(s_cur, pf);
-    accumulate(vbuf[j & 1], pf);
+    accumulate(vbuf(parity), pf);
   };
   using plain_t = std::integral_constant<bool, false>;
   using masked_t = std::integral_constant<bool, true>;
+  using even_t = std::integral_constant<int, 0>;
+  using odd_t = std::integral_constant<int, 1>;
 
   // Tile 0 sets the running max exactly (from the diagonal term, if any, and the tile).
   f32x4_t sa[QB][4], sb[QB][4];
@@ -353,7 +361,7 @@ void attn_bf16_kernel(AttnArgs a) {
     m0[qb] = m_run[qb];
     m_run[qb] = 0.f;
   }
-  scores(kbuf[0], sa);
+  scores(kbuf0, sa);
   bias_mask(0, sa);
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
@@ -367,20 +375,20 @@ void attn_bf16_kernel(AttnArgs a) {
       sa[qb][k] -= m_new;
     }
   }
-  int j = 0;
+  int j = 0;  // always even at the top of these loops
   for (; j + 2 < nkt && j + 2 < a.slow_from; j += 2) {
-    step(plain_t{}, j, sa, sb);
-    step(plain_t{}, j + 1, sb, sa);
+    step(even_t{}, plain_t{}, j, sa, sb);
+    step(odd_t{}, plain_t{}, j + 1, sb, sa);
   }
   for (; j + 2 < nkt; j += 2) {
-    step(masked_t{}, j, sa, sb);
-    step(masked_t{}, j + 1, sb, sa);
+    step(even_t{}, masked_t{}, j, sa, sb);
+    step(odd_t{}, masked_t{}, j + 1, sb, sa);
   }
   if (j + 1 < nkt) {
-    step(masked_t{}, j, sa, sb);
-    last(j + 1, sb);
+    step(even_t{}, masked_t{}, j, sa, sb);
+    last(odd_t{}, sb);
   } else {
-    last(j, sa);
+    last(even_t{}, sa);
   }
 
   // ---- epilogue: O / l ----
