@@ -38,7 +38,7 @@ def commands(out: str = LIB, extra: list[str] | None = None) -> list[list[str]]:
     for src in HIP_SOURCES:
         obj = os.path.join(objdir, src + ".o")
         cmds.append([hipcc(), "-x", "hip", f"--offload-arch={ARCH}", *common,
-                     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-fno-honor-nans",
                      "-c", os.path.join(CSRC, src), "-o", obj, *extra])
         objs.append(obj)
     for src in CXX_SOURCES:

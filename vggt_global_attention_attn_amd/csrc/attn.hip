@@ -71,18 +71,9 @@ struct AttnArgs {
   IndexGeom g;
 };
 
-// Plain v_max_f32 / v_max3_f32: scores are never NaN, and fmaxf would add canonicalising
-// moves and does not fuse into max3 on its own.
-__device__ __forceinline__ float vmax(float a, float b) {
-  float r;
-  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
-  return r;
-}
-__device__ __forceinline__ float max3(float a, float b, float c) {
-  float r;
-  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-  return r;
-}
+// This file is compiled with -fno-honor-nans (scores are never NaN; infinities are honoured),
+// so fmaxf lowers to plain v_max_f32 and chains of it fuse into v_max3_f32.
+__device__ __forceinline__ float vmax(float a, float b) { return fmaxf(a, b); }
 
 // Lanes l, l^16, l^32 and l^48 hold the same query.  v_permlane16_swap(x, x) leaves each
 // lane holding its own value and its xor-16 partner's in the two results; v_permlane32_swap
@@ -246,15 +237,15 @@ void attn_bf16_kernel(AttnArgs a) {
       }
     }
   };
+  // In-lane max as two independent max3 chains, then the lane-group exchange.
   auto row_max = [&](const f32x4_t (&s)[4]) {
-    float mx = max3(s[0][0], s[0][1], s[0][2]);
-    mx = max3(mx, s[0][3], s[1][0]);
-    mx = max3(mx, s[1][1], s[1][2]);
-    mx = max3(mx, s[1][3], s[2][0]);
-    mx = max3(mx, s[2][1], s[2][2]);
-    mx = max3(mx, s[2][3], s[3][0]);
-    mx = max3(mx, s[3][1], s[3][2]);
-    return group_max(vmax(mx, s[3][3]));
+    float a = fmaxf(fmaxf(s[0][0], s[0][1]), s[0][2]);
+    float b = fmaxf(fmaxf(s[2][0], s[2][1]), s[2][2]);
+    a = fmaxf(fmaxf(a, s[0][3]), s[1][0]);
+    b = fmaxf(fmaxf(b, s[2][3]), s[3][0]);
+    a = fmaxf(fmaxf(a, s[1][1]), s[1][2]);
+    b = fmaxf(fmaxf(b, s[3][1]), s[3][2]);
+    return group_max(fmaxf(fmaxf(a, s[1][3]), fmaxf(b, s[3][3])));
   };
   // Raise the running max by d >= 0 (scores of the tile in hand are relative to the old m).
   auto raise_max = [&](int qb, float d, f32x4_t (&s)[4]) {
