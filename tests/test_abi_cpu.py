@@ -95,6 +95,7 @@ def test_config5_sizes(va):
     (dict(g2f=True, mean=True), "EINVAL"),
     (dict(in_dtype="fp32", out_dtype="bf16"), "EINVAL"),
     (dict(flags=1 << 7), "EINVAL"),
+    (dict(flags=1 << 6), "EINVAL"),
     (dict(frames=0), "EINVAL"),
     (dict(heads=0), "EINVAL"),
     (dict(frames=6000, grid_h=37, grid_w=37), "EINVAL"),  # 8.2M tokens > limit

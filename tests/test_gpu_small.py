@@ -201,3 +201,51 @@ def test_error_codes(lib):
     assert L.vggt_attn_forward(h, P(q), P(k), P(v), P(out), P(ws), nbytes, stream) == 0
     assert L.vggt_attn_last_error() == b""
     torch.cuda.synchronize()
+
+
+def _rising(desc, seed, spike=None):
+    """bf16 inputs whose logits grow along the key sequence (every later tile raises the running
+    max), optionally with one key scaled up to a logit far above everything else."""
+    from synth import bf16_bits_to_f32, f32_to_bf16_bits
+    q, k, v = inputs_for(desc, "bf16", seed=seed)
+    kf = bf16_bits_to_f32(k)
+    ramp = np.linspace(0.2, 4.0, desc.T, dtype=np.float32)[None, :, None]
+    kf = kf * ramp
+    if spike is not None:
+        t, factor = spike
+        kf[:, t, :] = bf16_bits_to_f32(q)[:, 0, :] * factor  # aligned with query 0: huge logit for row 0
+    return q, f32_to_bf16_bits(kf), v
+
+
+@pytest.mark.parametrize("desc,label", [
+    (Desc(6, 13, 11, 2, sigma=1), "dense"),
+    (Desc(6, 13, 11, 2, sigma=4, diag=True, mean=True), "sga4-enh"),
+    (Desc(4, 37, 37, 2, g2f=True), "g2f"),
+], ids=["dense", "sga4-enh", "g2f"])
+def test_running_max_catch_up(lib, desc, label):
+    """Logits that keep rising along the keys force the rare exact catch-up of the running max
+    (a score more than an octave above it) in many tiles; a spiked key drives exp2 past the
+    float range before the catch-up.  Both must still match the oracle."""
+    q, k, v = _rising(desc, seed=11)
+    _, got, _, _ = run(lib, desc, q, k, v)
+    ref = oracle.attention(q, k, v, desc, workers=4)
+    assert_close(got, ref, fp32=False, label=label + "/rising")
+    last_frame_token = desc.T - 3
+    q, k, v = _rising(desc, seed=12, spike=(last_frame_token, 40.0))
+    _, got, _, _ = run(lib, desc, q, k, v)
+    ref = oracle.attention(q, k, v, desc, workers=4)
+    assert_close(got, ref, fp32=False, label=label + "/spike")
+
+
+@pytest.mark.parametrize("desc,label", [CASES[i] for i in (2, 4, 5, 7, 9)], ids=[CASES[i][1] for i in (2, 4, 5, 7, 9)])
+def test_parity_prescaled_q(lib, desc, label):
+    """The opt-in PRESCALE_Q form (Q scaled by tau*log2(e) and rounded to bf16 once) on the
+    seeded workload inputs."""
+    import torch
+    q, k, v = inputs_for(desc, "bf16", seed=13)
+    plan = lib.Plan(**plan_kwargs(desc), prescale_q=True)
+    out = plan.new_output()
+    plan.forward(to_device(q), to_device(k), to_device(v), out, plan.new_workspace())
+    torch.cuda.synchronize()
+    ref = oracle.attention(q, k, v, desc, workers=4)
+    assert_close(out.float().cpu().numpy(), ref, fp32=False, label=label + "/prescaled")

@@ -13,7 +13,7 @@ import numpy as np
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libvggt_attn.so")
 
 BF16, FP32 = 0, 1
-G2F, REF_DENSE, DIAG, MEAN, MEAN_COUNT = 1, 2, 4, 8, 16
+G2F, REF_DENSE, DIAG, MEAN, MEAN_COUNT, PRESCALE_Q = 1, 2, 4, 8, 16, 32
 
 STATUS = {0: "OK", -1: "EINVAL", -2: "EUNSUPPORTED", -3: "ENOSPC", -4: "EALIGN", -5: "EALIAS", -6: "EHIP"}
 
@@ -106,10 +106,12 @@ class Plan:
     def __init__(self, frames: int, grid_h: int, grid_w: int, heads: int, head_dim: int = 64,
                  n_special: int = 5, sigma: int = 1, ref_dense: bool = True, diag: bool = False,
                  mean: bool = False, mean_count: bool = False, g2f: bool = False,
-                 in_dtype: str = "bf16", out_dtype: str = "fp32", flags: int | None = None):
+                 in_dtype: str = "bf16", out_dtype: str = "fp32", prescale_q: bool = False,
+                 flags: int | None = None):
         if flags is None:
             flags = ((G2F if g2f else 0) | (REF_DENSE if ref_dense else 0) | (DIAG if diag else 0) |
-                     (MEAN if mean else 0) | (MEAN_COUNT if mean_count else 0))
+                     (MEAN if mean else 0) | (MEAN_COUNT if mean_count else 0) |
+                     (PRESCALE_Q if prescale_q else 0))
         self._h = ctypes.c_void_p()
         self.frames, self.grid_h, self.grid_w, self.heads, self.head_dim = frames, grid_h, grid_w, heads, head_dim
         self.n_special, self.sigma, self.flags = n_special, sigma, flags

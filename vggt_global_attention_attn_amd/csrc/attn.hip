@@ -31,6 +31,9 @@
 #ifndef VGGT_GLOBAL_WPE
 #define VGGT_GLOBAL_WPE 2
 #endif
+#ifndef VGGT_OVERFLOW_CHECK
+#define VGGT_OVERFLOW_CHECK 1
+#endif
 #ifndef VGGT_G2F_QB
 #define VGGT_G2F_QB 2
 #endif
@@ -91,9 +94,10 @@ __device__ __forceinline__ float group_sum(float x) {
   return __uint_as_float(q[0]) + __uint_as_float(q[1]);
 }
 
-template <int QB, int WPE, bool OUT_BF16>
+template <int QB, int WPE, bool OUT_BF16, bool PRESCALE_Q>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 void attn_bf16_kernel(AttnArgs a) {
+  constexpr bool kExactScale = !PRESCALE_Q;
   constexpr int WQ = 16 * QB;  // query rows per wave
   constexpr int BM = 4 * WQ;   // query rows per work-group
   // Two K tiles and two V tiles of 64 rows x 128 bytes; 16-byte chunks XOR-swizzled by row so
@@ -140,7 +144,14 @@ void attn_bf16_kernel(AttnArgs a) {
   bf16x8_t qf[QB][2];
   float m_run[QB], l_run[QB];  // running max (log2 units) and lane-partial row sum
   f32x4_t o[QB][4];
+  // Two ways to reach log2 units.  Exact (default): Q is used as given, scores and the running
+  // max are in units of q.k, and the exp2 argument is multiplied by c = tau*log2(e).
+  // PRESCALE_Q (opt-in plan flag): Q is scaled by c once and rounded to bf16, which saves that
+  // multiply per score but perturbs every logit of a row by a relative 2^-9 -- coherently
+  // across the row, unlike the independent rounding of P.
   const float c = a.c_log2;
+  const float qscale = kExactScale ? 1.f : c;   // applied to Q at load
+  const float sc = kExactScale ? c : 1.f;       // applied to scores at the exp
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int64_t t = wrow0 + qb * 16 + l16;
@@ -157,7 +168,7 @@ void attn_bf16_kernel(AttnArgs a) {
       bf16x8_t v;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float q0 = __uint_as_float(qw[i] << 16) * c, q1 = __uint_as_float(qw[i] & 0xffff0000u) * c;
+        const float q0 = __uint_as_float(qw[i] << 16) * qscale, q1 = __uint_as_float(qw[i] & 0xffff0000u) * qscale;
         v[2 * i] = (__bf16)q0;
         v[2 * i + 1] = (__bf16)q1;
         // Diagonal self logit from the same scaled query the matrix core uses.
@@ -231,7 +242,7 @@ void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int key = j * kTile + k4 * 16 + grp * 4 + i;
-        const float add = key >= a.nkeys ? -INFINITY : (key >= a.n_plain ? a.bias_log2 : 0.f);
+        const float add = key >= a.nkeys ? -INFINITY : (key >= a.n_plain ? (kExactScale ? a.bias_s : a.bias_log2) : 0.f);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) s[qb][k4][i] += add;
       }
@@ -250,7 +261,7 @@ void attn_bf16_kernel(AttnArgs a) {
   // Raise the running max by d >= 0 (scores of the tile in hand are relative to the old m).
   auto raise_max = [&](int qb, float d, f32x4_t (&s)[4]) {
     asm volatile("; rare rescale" ::);  // keeps this branch from being speculated into every tile
-    const float alpha = __builtin_amdgcn_exp2f(-d);
+    const float alpha = __builtin_amdgcn_exp2f(-d * sc);
     m_run[qb] += d;
     l_run[qb] *= alpha;
 #pragma unroll
@@ -314,7 +325,90 @@ void attn_bf16_kernel(AttnArgs a) {
   wait_tiles();
   __syncthreads();
 
-  // One pipelined step: finish tile j (scores s_cur) while the scores of tile j+1 are formed.
+  // K and V operand fragments of a tile: read once per step, shared by every query block.
+  auto k_frags = [&](const uint8_t* kb, bf16x8_t (&kf)[4][2]) {
+#pragma unroll
+    for (int k4 = 0; k4 < 4; ++k4) {
+      kf[k4][0] = lds_frag(kb, k4 * 16 + l16, grp);
+      kf[k4][1] = lds_frag(kb, k4 * 16 + l16, 4 + grp);
+    }
+  };
+  auto scores_qb = [&](const bf16x8_t (&kf)[4][2], int qb, f32x4_t (&s)[4]) {
+    const float mneg = -m_run[qb];
+#pragma unroll
+    for (int k4 = 0; k4 < 4; ++k4) {
+      f32x4_t acc = {mneg, mneg, mneg, mneg};
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[k4][0], qf[qb][0], acc, 0, 0, 0);
+      s[k4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[k4][1], qf[qb][1], acc, 0, 0, 0);
+    }
+  };
+  auto probs_qb = [&](int qb, const f32x4_t (&s)[4], bf16x8_t (&pf)[2]) {
+    uint32_t bits = 0;
+    float l = l_run[qb];
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      const f32x4_t& s0 = s[2 * h2];
+      const f32x4_t& s1 = s[2 * h2 + 1];
+      const bf16x8_t pv = {
+          (__bf16)__builtin_amdgcn_exp2f(s0[0] * sc), (__bf16)__builtin_amdgcn_exp2f(s0[1] * sc),
+          (__bf16)__builtin_amdgcn_exp2f(s0[2] * sc), (__bf16)__builtin_amdgcn_exp2f(s0[3] * sc),
+          (__bf16)__builtin_amdgcn_exp2f(s1[0] * sc), (__bf16)__builtin_amdgcn_exp2f(s1[1] * sc),
+          (__bf16)__builtin_amdgcn_exp2f(s1[2] * sc), (__bf16)__builtin_amdgcn_exp2f(s1[3] * sc)};
+      pf[h2] = pv;
+      const uint4 w = __builtin_bit_cast(uint4, pv);
+      bits |= w.x | w.y | w.z | w.w;
+      l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pv, pv, 0, 1), kOnes2, l, false);
+      l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pv, pv, 2, 3), kOnes2, l, false);
+      l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pv, pv, 4, 5), kOnes2, l, false);
+      l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pv, pv, 6, 7), kOnes2, l, false);
+    }
+    l_run[qb] = l;
+    return bits;
+  };
+  auto accumulate_qb = [&](const bf16x8_t (&vf)[4][2], int qb, const bf16x8_t (&pf)[2]) {
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      o[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[db][0], pf[0], o[qb][db], 0, 0, 0);
+      o[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[db][1], pf[1], o[qb][db], 0, 0, 0);
+    }
+  };
+  // Softmax of query block qb of the tile in hand (scores s relative to the running max), with
+  // the block's next-tile scores formed on the matrix cores in the same stretch of code.
+#if VGGT_OVERFLOW_CHECK
+  // Overflow check after the exps: every p >= 0, so some p >= 2 (a score above the running max
+  // by more than one octave) exactly when bit 14 of some packed bf16 half is set.  In that rare
+  // case the max is raised exactly and the block is redone; otherwise p < 2 needs no rescale.
+  auto block = [&](const bf16x8_t (&kf)[4][2], int qb, f32x4_t (&s_cur)[4], f32x4_t (&s_next)[4],
+                   bf16x8_t (&pf)[2], bool next) {
+    if (next) scores_qb(kf, qb, s_next);
+    const float l_prev = l_run[qb];
+    if (__builtin_amdgcn_ballot_w64((probs_qb(qb, s_cur, pf) & 0x40004000u) != 0) != 0) {
+      asm volatile("; rare rescale" ::);
+      const float d = vmax(row_max(s_cur), 0.f);
+      const float alpha = __builtin_amdgcn_exp2f(-d * sc);
+      m_run[qb] += d;
+      l_run[qb] = l_prev * alpha;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        o[qb][k] *= alpha;
+        s_cur[k] -= d;
+        if (next) s_next[k] -= d;  // formed against the old max
+      }
+      probs_qb(qb, s_cur, pf);
+    }
+  };
+#else
+  auto block = [&](const bf16x8_t (&kf)[4][2], int qb, f32x4_t (&s_cur)[4], f32x4_t (&s_next)[4],
+                   bf16x8_t (&pf)[2], bool next) {
+    const float mx = row_max(s_cur);
+    if (__builtin_amdgcn_ballot_w64(mx * sc > kLazyRescale) != 0) raise_max(qb, vmax(mx, 0.f), s_cur);
+    if (next) scores_qb(kf, qb, s_next);
+    probs_qb(qb, s_cur, pf);
+  };
+#endif
+
+  // One pipelined step: finish tile j (scores s_cur) while the scores of tile j+1 are formed,
+  // query block by query block so that every stretch of code mixes matrix-core and VALU work.
   // P = j & 1 is a compile-time constant, so every LDS buffer is static.  MASK = tile j+1 may
   // hold mean keys or padding (kept out of the steady-state loop, where the compiler would
   // otherwise if-convert the bias into every tile).
@@ -324,20 +418,28 @@ void attn_bf16_kernel(AttnArgs a) {
     using other_t = std::integral_constant<int, P ^ 1>;
     async_tile(kseg, min(j + 2, nkt - 1), kbuf(same_t{}));
     async_tile(vseg, j + 1, vbuf(other_t{}));
-    update_max(s_cur);
-    scores(kbuf(other_t{}), s_next);
-    bf16x8_t pf[QB][2];
-    probabilities(s_cur, pf);
-    accumulate(vbuf(same_t{}), pf);
+    bf16x8_t kf[4][2], vf[4][2];
+    k_frags(kbuf(other_t{}), kf);
+    k_frags(vbuf(same_t{}), vf);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      bf16x8_t pf[2];
+      block(kf, qb, s_cur[qb], s_next[qb], pf, true);
+      accumulate_qb(vf, qb, pf);
+    }
     if constexpr (decltype(mask_tag)::value) bias_mask(j + 1, s_next);
     wait_tiles();
     __syncthreads();
   };
   auto last = [&](auto parity, f32x4_t (&s_cur)[QB][4]) {
-    update_max(s_cur);
-    bf16x8_t pf[QB][2];
-    probabilities(s_cur, pf);
-    accumulate(vbuf(parity), pf);
+    bf16x8_t kf[4][2], vf[4][2];
+    k_frags(vbuf(parity), vf);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      bf16x8_t pf[2];
+      block(kf, qb, s_cur[qb], s_cur[qb], pf, false);
+      accumulate_qb(vf, qb, pf);
+    }
   };
   using plain_t = std::integral_constant<bool, false>;
   using masked_t = std::integral_constant<bool, true>;
@@ -357,7 +459,7 @@ void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const float m_new = vmax(m0[qb], row_max(sa[qb]));  // finite: tile 0 holds a valid key
-    const float alpha = __builtin_amdgcn_exp2f(m0[qb] - m_new);
+    const float alpha = __builtin_amdgcn_exp2f((m0[qb] - m_new) * sc);
     m_run[qb] = m_new;
     l_run[qb] *= alpha;
 #pragma unroll
@@ -547,13 +649,17 @@ hipError_t launch_attend(const vggt_attn_plan_s& p, const void* q, const void* k
   }
   const unsigned blocks = unsigned(int64_t(a.qtiles) * p.heads);
   const bool ob = p.out_dtype == VGGT_ATTN_BF16;
-  if (p.g2f) {
-    if (ob) hipLaunchKernelGGL((attn_bf16_kernel<QBf, WPEf, true>), dim3(blocks), dim3(256), 0, stream, a);
-    else hipLaunchKernelGGL((attn_bf16_kernel<QBf, WPEf, false>), dim3(blocks), dim3(256), 0, stream, a);
-  } else {
-    if (ob) hipLaunchKernelGGL((attn_bf16_kernel<QBg, WPEg, true>), dim3(blocks), dim3(256), 0, stream, a);
-    else hipLaunchKernelGGL((attn_bf16_kernel<QBg, WPEg, false>), dim3(blocks), dim3(256), 0, stream, a);
-  }
+  const bool pre = p.prescale_q;
+#define VGGT_LAUNCH(QB_, WPE_)                                                                       \
+  do {                                                                                              \
+    if (ob && pre) hipLaunchKernelGGL((attn_bf16_kernel<QB_, WPE_, true, true>), dim3(blocks), dim3(256), 0, stream, a);    \
+    else if (ob) hipLaunchKernelGGL((attn_bf16_kernel<QB_, WPE_, true, false>), dim3(blocks), dim3(256), 0, stream, a);     \
+    else if (pre) hipLaunchKernelGGL((attn_bf16_kernel<QB_, WPE_, false, true>), dim3(blocks), dim3(256), 0, stream, a);    \
+    else hipLaunchKernelGGL((attn_bf16_kernel<QB_, WPE_, false, false>), dim3(blocks), dim3(256), 0, stream, a);            \
+  } while (0)
+  if (p.g2f) VGGT_LAUNCH(QBf, WPEf);
+  else VGGT_LAUNCH(QBg, WPEg);
+#undef VGGT_LAUNCH
   return hipGetLastError();
 }
 

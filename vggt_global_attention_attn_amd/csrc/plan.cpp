@@ -49,7 +49,7 @@ int build_plan(vggt_attn_plan_s* p, int frames, int grid_h, int grid_w, int n_sp
   if (!window_of(sigma, &s_h, &s_w))
     return fail(err, VGGT_ATTN_EINVAL, "sigma %lld not in {1, 2, 4, 6, 9}", sigma);
   const unsigned known = VGGT_ATTN_G2F | VGGT_ATTN_REF_DENSE | VGGT_ATTN_DIAG | VGGT_ATTN_MEAN |
-                         VGGT_ATTN_MEAN_COUNT;
+                         VGGT_ATTN_MEAN_COUNT | VGGT_ATTN_PRESCALE_Q;
   if (flags & ~known) return fail(err, VGGT_ATTN_EINVAL, "unknown flag bits 0x%llx", flags & ~known);
   const bool g2f = flags & VGGT_ATTN_G2F;
   if (g2f && (sigma != 1 || (flags & (VGGT_ATTN_DIAG | VGGT_ATTN_MEAN))))
@@ -75,6 +75,7 @@ int build_plan(vggt_attn_plan_s* p, int frames, int grid_h, int grid_w, int n_sp
   p->diag = (flags & VGGT_ATTN_DIAG) && p->subsampled;
   p->mean = (flags & VGGT_ATTN_MEAN) && p->subsampled;
   p->mean_count = flags & VGGT_ATTN_MEAN_COUNT;
+  p->prescale_q = flags & VGGT_ATTN_PRESCALE_Q;
   p->s_h = s_h; p->s_w = s_w;
   p->L = int(L); p->P = int(P); p->T = T;
   p->kh = int(ceil_div(grid_h, s_h));

@@ -38,7 +38,7 @@ struct vggt_attn_plan_s {
   unsigned flags;
   int in_dtype, out_dtype;
   // derived
-  bool g2f, ref_dense, diag, mean, mean_count, subsampled;
+  bool g2f, ref_dense, diag, mean, mean_count, subsampled, prescale_q;
   int s_h, s_w, L, P, kh, kw, kept;
   int64_t T;
   int64_t dropped;        // |D_f| of a compressed frame
