@@ -31,9 +31,6 @@
 #ifndef VGGT_GLOBAL_WPE
 #define VGGT_GLOBAL_WPE 2
 #endif
-#ifndef VGGT_OVERFLOW_CHECK
-#define VGGT_OVERFLOW_CHECK 1
-#endif
 #ifndef VGGT_G2F_QB
 #define VGGT_G2F_QB 2
 #endif
@@ -45,7 +42,6 @@ namespace vggt {
 namespace {
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-constexpr float kLazyRescale = 8.f;  // log2 units
 // s_waitcnt immediate for vmcnt(0) with expcnt and lgkmcnt left at their maxima (gfx9 encoding).
 constexpr int kWaitVmcnt0 = 0x0F70;
 constexpr bf16x2_t kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
@@ -218,114 +214,7 @@ void attn_bf16_kernel(AttnArgs a) {
     return *reinterpret_cast<const bf16x8_t*>(&buf[row * 128 + ((ch ^ (row & 7)) << 4)]);
   };
 
-  // S'^T = K Q'^T - m for 64 keys x WQ queries: the running max enters as the accumulator's
-  // initial value, so the scores leave the matrix core already shifted (log2 units).
-  auto scores = [&](const uint8_t* kb, f32x4_t (&s)[QB][4]) {
-#pragma unroll
-    for (int k4 = 0; k4 < 4; ++k4) {
-      const int row = k4 * 16 + l16;
-      const bf16x8_t k0 = lds_frag(kb, row, grp), k1 = lds_frag(kb, row, 4 + grp);
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        const float mneg = -m_run[qb];
-        f32x4_t acc = {mneg, mneg, mneg, mneg};
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qf[qb][0], acc, 0, 0, 0);
-        s[qb][k4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qf[qb][1], acc, 0, 0, 0);
-      }
-    }
-  };
-  // Mean-key bias and padding mask, only for the last tiles of the segment.
-  auto bias_mask = [&](int j, f32x4_t (&s)[QB][4]) {
-    if (j < a.slow_from) return;
-#pragma unroll
-    for (int k4 = 0; k4 < 4; ++k4) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = j * kTile + k4 * 16 + grp * 4 + i;
-        const float add = key >= a.nkeys ? -INFINITY : (key >= a.n_plain ? (kExactScale ? a.bias_s : a.bias_log2) : 0.f);
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) s[qb][k4][i] += add;
-      }
-    }
-  };
-  // In-lane max as two independent max3 chains, then the lane-group exchange.
-  auto row_max = [&](const f32x4_t (&s)[4]) {
-    float a = fmaxf(fmaxf(s[0][0], s[0][1]), s[0][2]);
-    float b = fmaxf(fmaxf(s[2][0], s[2][1]), s[2][2]);
-    a = fmaxf(fmaxf(a, s[0][3]), s[1][0]);
-    b = fmaxf(fmaxf(b, s[2][3]), s[3][0]);
-    a = fmaxf(fmaxf(a, s[1][1]), s[1][2]);
-    b = fmaxf(fmaxf(b, s[3][1]), s[3][2]);
-    return group_max(fmaxf(fmaxf(a, s[1][3]), fmaxf(b, s[3][3])));
-  };
-  // Raise the running max by d >= 0 (scores of the tile in hand are relative to the old m).
-  auto raise_max = [&](int qb, float d, f32x4_t (&s)[4]) {
-    asm volatile("; rare rescale" ::);  // keeps this branch from being speculated into every tile
-    const float alpha = __builtin_amdgcn_exp2f(-d * sc);
-    m_run[qb] += d;
-    l_run[qb] *= alpha;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      o[qb][k] *= alpha;
-      s[k] -= d;
-    }
-  };
-  // Lazy rescale: m is only raised when a tile's (shifted) max exceeds 2^8.  Until then
-  // p = 2^s' <= 2^8, exact in bf16's range and in the float32 sums, and the O/l rescale (the
-  // costliest VALU step) is skipped; O/l is the same quotient either way.
-  auto update_max = [&](f32x4_t (&s)[QB][4]) {
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      const float mx = row_max(s[qb]);
-      if (__builtin_amdgcn_ballot_w64(mx > kLazyRescale) != 0) raise_max(qb, vmax(mx, 0.f), s[qb]);
-    }
-  };
-  // p = 2^s' rounded to bf16, already in the B-operand layout of the PV product; the row sum
-  // uses the same rounded weights.
-  auto probabilities = [&](const f32x4_t (&s)[QB][4], bf16x8_t (&pf)[QB][2]) {
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      float l = l_run[qb];
-#pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
-        const f32x4_t& s0 = s[qb][2 * h2];
-        const f32x4_t& s1 = s[qb][2 * h2 + 1];
-        const bf16x8_t pv = {
-            (__bf16)__builtin_amdgcn_exp2f(s0[0]), (__bf16)__builtin_amdgcn_exp2f(s0[1]),
-            (__bf16)__builtin_amdgcn_exp2f(s0[2]), (__bf16)__builtin_amdgcn_exp2f(s0[3]),
-            (__bf16)__builtin_amdgcn_exp2f(s1[0]), (__bf16)__builtin_amdgcn_exp2f(s1[1]),
-            (__bf16)__builtin_amdgcn_exp2f(s1[2]), (__bf16)__builtin_amdgcn_exp2f(s1[3])};
-        pf[qb][h2] = pv;
-        l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pv, pv, 0, 1), kOnes2, l, false);
-        l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pv, pv, 2, 3), kOnes2, l, false);
-        l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pv, pv, 4, 5), kOnes2, l, false);
-        l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pv, pv, 6, 7), kOnes2, l, false);
-      }
-      l_run[qb] = l;
-    }
-  };
-  // O^T += V^T P^T.
-  auto accumulate = [&](const uint8_t* vb, const bf16x8_t (&pf)[QB][2]) {
-#pragma unroll
-    for (int db = 0; db < 4; ++db) {
-      const int row = db * 16 + l16;
-      const bf16x8_t v0 = lds_frag(vb, row, grp), v1 = lds_frag(vb, row, 4 + grp);
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        o[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v0, pf[qb][0], o[qb][db], 0, 0, 0);
-        o[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v1, pf[qb][1], o[qb][db], 0, 0, 0);
-      }
-    }
-  };
-
-  const int nkt = a.nktiles;
-  async_tile(kseg, 0, kbuf0);
-  async_tile(vseg, 0, vbuf0);
-  if (nkt > 1) async_tile(kseg, 1, kbuf1);
-  wait_tiles();
-  __syncthreads();
-
-  // K and V operand fragments of a tile: read once per step, shared by every query block.
+  // K (or V) operand fragments of a tile: read once per step, shared by every query block.
   auto k_frags = [&](const uint8_t* kb, bf16x8_t (&kf)[4][2]) {
 #pragma unroll
     for (int k4 = 0; k4 < 4; ++k4) {
@@ -333,27 +222,60 @@ void attn_bf16_kernel(AttnArgs a) {
       kf[k4][1] = lds_frag(kb, k4 * 16 + l16, 4 + grp);
     }
   };
+  // S^T = K Q^T for 64 keys x the 16 queries of block qb: s[k4][i] is key k4*16 + grp*4 + i.
+  // Exact mode starts each two-MFMA chain from a zero accumulator (an inline constant, so the
+  // first MFMA reads no accumulator registers and the second takes its input straight from the
+  // first); the running max is applied in the exp argument.  PRESCALE_Q mode starts it from
+  // -m, so the scores leave the matrix core already shifted.
   auto scores_qb = [&](const bf16x8_t (&kf)[4][2], int qb, f32x4_t (&s)[4]) {
     const float mneg = -m_run[qb];
 #pragma unroll
     for (int k4 = 0; k4 < 4; ++k4) {
-      f32x4_t acc = {mneg, mneg, mneg, mneg};
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (PRESCALE_Q) acc = f32x4_t{mneg, mneg, mneg, mneg};
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[k4][0], qf[qb][0], acc, 0, 0, 0);
       s[k4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[k4][1], qf[qb][1], acc, 0, 0, 0);
     }
   };
+  // Mean-key bias and padding mask, only for the last tiles of the segment.
+  auto bias_mask = [&](int j, f32x4_t (&s)[QB][4]) {
+    if (j < a.slow_from) return;
+    const float bias = PRESCALE_Q ? a.bias_log2 : a.bias_s;
+#pragma unroll
+    for (int k4 = 0; k4 < 4; ++k4) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int key = j * kTile + k4 * 16 + grp * 4 + i;
+        const float add = key >= a.nkeys ? -INFINITY : (key >= a.n_plain ? bias : 0.f);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) s[qb][k4][i] += add;
+      }
+    }
+  };
+  // In-lane max as two independent max3 chains, then the lane-group exchange.
+  auto row_max = [&](const f32x4_t (&s)[4]) {
+    float x = fmaxf(fmaxf(s[0][0], s[0][1]), s[0][2]);
+    float y = fmaxf(fmaxf(s[2][0], s[2][1]), s[2][2]);
+    x = fmaxf(fmaxf(x, s[0][3]), s[1][0]);
+    y = fmaxf(fmaxf(y, s[2][3]), s[3][0]);
+    x = fmaxf(fmaxf(x, s[1][1]), s[1][2]);
+    y = fmaxf(fmaxf(y, s[3][1]), s[3][2]);
+    return group_max(fmaxf(fmaxf(x, s[1][3]), fmaxf(y, s[3][3])));
+  };
+  // p = 2^(c (s - m)) (exact) or 2^s' (PRESCALE_Q) rounded to bf16, already in the B-operand
+  // layout of the PV product; the row sum uses the same rounded weights.  Returns the OR of the
+  // packed bf16 words: every p >= 0, so some p >= 2 (a score more than one octave above the
+  // running max) exactly when bit 14 of some half is set.
   auto probs_qb = [&](int qb, const f32x4_t (&s)[4], bf16x8_t (&pf)[2]) {
+    const float off = PRESCALE_Q ? 0.f : -m_run[qb] * c;
+    auto e = [&](float x) { return (__bf16)__builtin_amdgcn_exp2f(PRESCALE_Q ? x : fmaf(x, c, off)); };
     uint32_t bits = 0;
     float l = l_run[qb];
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2) {
       const f32x4_t& s0 = s[2 * h2];
       const f32x4_t& s1 = s[2 * h2 + 1];
-      const bf16x8_t pv = {
-          (__bf16)__builtin_amdgcn_exp2f(s0[0] * sc), (__bf16)__builtin_amdgcn_exp2f(s0[1] * sc),
-          (__bf16)__builtin_amdgcn_exp2f(s0[2] * sc), (__bf16)__builtin_amdgcn_exp2f(s0[3] * sc),
-          (__bf16)__builtin_amdgcn_exp2f(s1[0] * sc), (__bf16)__builtin_amdgcn_exp2f(s1[1] * sc),
-          (__bf16)__builtin_amdgcn_exp2f(s1[2] * sc), (__bf16)__builtin_amdgcn_exp2f(s1[3] * sc)};
+      const bf16x8_t pv = {e(s0[0]), e(s0[1]), e(s0[2]), e(s0[3]), e(s1[0]), e(s1[1]), e(s1[2]), e(s1[3])};
       pf[h2] = pv;
       const uint4 w = __builtin_bit_cast(uint4, pv);
       bits |= w.x | w.y | w.z | w.w;
@@ -372,40 +294,42 @@ void attn_bf16_kernel(AttnArgs a) {
       o[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[db][1], pf[1], o[qb][db], 0, 0, 0);
     }
   };
-  // Softmax of query block qb of the tile in hand (scores s relative to the running max), with
-  // the block's next-tile scores formed on the matrix cores in the same stretch of code.
-#if VGGT_OVERFLOW_CHECK
-  // Overflow check after the exps: every p >= 0, so some p >= 2 (a score above the running max
-  // by more than one octave) exactly when bit 14 of some packed bf16 half is set.  In that rare
-  // case the max is raised exactly and the block is redone; otherwise p < 2 needs no rescale.
+  // Softmax of query block qb of the tile in hand, with the block's next-tile scores formed on
+  // the matrix cores in the same stretch of code.  Lazy running max: weights are taken against
+  // the current m; only if some weight reaches 2 is m raised exactly to the row max (O and l
+  // rescaled) and the block redone, so in the steady state no per-score max and no rescale run.
   auto block = [&](const bf16x8_t (&kf)[4][2], int qb, f32x4_t (&s_cur)[4], f32x4_t (&s_next)[4],
                    bf16x8_t (&pf)[2], bool next) {
     if (next) scores_qb(kf, qb, s_next);
     const float l_prev = l_run[qb];
-    if (__builtin_amdgcn_ballot_w64((probs_qb(qb, s_cur, pf) & 0x40004000u) != 0) != 0) {
-      asm volatile("; rare rescale" ::);
-      const float d = vmax(row_max(s_cur), 0.f);
+    const uint32_t bits = probs_qb(qb, s_cur, pf);
+    if (__builtin_amdgcn_ballot_w64((bits & 0x40004000u) != 0) != 0) {
+      asm volatile("; rare rescale" ::);  // keeps this branch from being speculated into every tile
+      // Exact mode: scores are absolute (q.k), d is the raise of m.  PRESCALE_Q: scores are
+      // relative to m (log2 units), so they and the already formed next-tile scores shift too.
+      const float mx = row_max(s_cur);
+      const float d = PRESCALE_Q ? vmax(mx, 0.f) : vmax(mx - m_run[qb], 0.f);
       const float alpha = __builtin_amdgcn_exp2f(-d * sc);
       m_run[qb] += d;
       l_run[qb] = l_prev * alpha;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         o[qb][k] *= alpha;
-        s_cur[k] -= d;
-        if (next) s_next[k] -= d;  // formed against the old max
+        if constexpr (PRESCALE_Q) {
+          s_cur[k] -= d;
+          if (next) s_next[k] -= d;
+        }
       }
       probs_qb(qb, s_cur, pf);
     }
   };
-#else
-  auto block = [&](const bf16x8_t (&kf)[4][2], int qb, f32x4_t (&s_cur)[4], f32x4_t (&s_next)[4],
-                   bf16x8_t (&pf)[2], bool next) {
-    const float mx = row_max(s_cur);
-    if (__builtin_amdgcn_ballot_w64(mx * sc > kLazyRescale) != 0) raise_max(qb, vmax(mx, 0.f), s_cur);
-    if (next) scores_qb(kf, qb, s_next);
-    probs_qb(qb, s_cur, pf);
-  };
-#endif
+
+  const int nkt = a.nktiles;
+  async_tile(kseg, 0, kbuf0);
+  async_tile(vseg, 0, vbuf0);
+  if (nkt > 1) async_tile(kseg, 1, kbuf1);
+  wait_tiles();
+  __syncthreads();
 
   // One pipelined step: finish tile j (scores s_cur) while the scores of tile j+1 are formed,
   // query block by query block so that every stretch of code mixes matrix-core and VALU work.
@@ -448,24 +372,28 @@ void attn_bf16_kernel(AttnArgs a) {
 
   // Tile 0 sets the running max exactly (from the diagonal term, if any, and the tile).
   f32x4_t sa[QB][4], sb[QB][4];
-  float m0[QB];
+  {
+    bf16x8_t kf[4][2];
+    k_frags(kbuf0, kf);
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    m0[qb] = m_run[qb];
-    m_run[qb] = 0.f;
+    for (int qb = 0; qb < QB; ++qb) {
+      const float m_self = m_run[qb];
+      m_run[qb] = 0.f;
+      scores_qb(kf, qb, sa[qb]);
+      m_run[qb] = m_self;
+    }
   }
-  scores(kbuf0, sa);
   bias_mask(0, sa);
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    const float m_new = vmax(m0[qb], row_max(sa[qb]));  // finite: tile 0 holds a valid key
-    const float alpha = __builtin_amdgcn_exp2f((m0[qb] - m_new) * sc);
+    const float m_new = vmax(m_run[qb], row_max(sa[qb]));  // finite: tile 0 holds a valid key
+    const float alpha = __builtin_amdgcn_exp2f((m_run[qb] - m_new) * sc);
     m_run[qb] = m_new;
     l_run[qb] *= alpha;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       o[qb][k] *= alpha;
-      sa[qb][k] -= m_new;
+      if constexpr (PRESCALE_Q) sa[qb][k] -= m_new;
     }
   }
   int j = 0;  // always even at the top of these loops
