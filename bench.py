@@ -47,6 +47,15 @@ WORKLOADS = {
                   "200 frames x 1374 tokens, 16 heads, d=64, bf16 in / fp32 out, SGA sigma=9 (3x3), diag + mean"),
 }
 
+# Reported beside the headline workload (same run, fewer steps).  The 200-frame pair runs G2F and
+# then SGA sigma 9 on the same tensors, the early/middle layer split.
+EXTRA_GROUPS = [
+    ("tiny-fp32", [dict(frames=4, grid_h=8, grid_w=8, heads=2, sigma=4, diag=True, mean=True)], "fp32"),
+    ("dense-32f", [WORKLOADS["dense-32f"][0]], "bf16"),
+    ("sga4-100f", [WORKLOADS["sga4-100f"][0]], "bf16"),
+    ("g2f+sga9-200f", [WORKLOADS["g2f-200f"][0], WORKLOADS["sga9-200f"][0]], "bf16"),
+]
+
 KERNEL_SOURCES = ("vggt_global_attention_attn_amd/csrc/attn.hip", "vggt_global_attention_attn_amd/csrc/device_common.h")
 TRAFFIC_FILE = "profiles/attn_{workload}_hbm_traffic.txt"
 
@@ -98,6 +107,63 @@ def gather_bytes(desc, c) -> int:
     return int(H * (rows_read + rows_written) * d * e * 2 + index)
 
 
+def time_calls(plans, tensors, outs, wss, steps, warmup):
+    """Average seconds per step (all plans' forwards) and per plan's attention launch."""
+    import torch
+    for _ in range(warmup):
+        for p, o, w in zip(plans, outs, wss):
+            p.forward(*tensors, o, w)
+    torch.cuda.synchronize()
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+            torch.cuda.Event(enable_timing=True)) for _ in plans] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for row in ev:
+        for (e0, e1, e2), p, o, w in zip(row, plans, outs, wss):
+            e0.record()
+            p.pack(tensors[1], tensors[2], w)
+            e1.record()
+            p.attend(*tensors, o, w)
+            e2.record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps
+    attn = [sum(row[i][1].elapsed_time(row[i][2]) for row in ev) / steps * 1e-3 for i in range(len(plans))]
+    return wall, attn
+
+
+def extra_workloads(dev, steps: int):
+    import numpy as np
+    import torch
+
+    import vggt_global_attention_attn_amd as va
+    from synth import make_qkv
+
+    results = []
+    for name, descs, dtype in EXTRA_GROUPS:
+        d0 = descs[0]
+        q, k, v = make_qkv(d0["frames"], d0["grid_h"], d0["grid_w"], 5, d0["heads"], 64, dtype, seed=0)
+        if dtype == "bf16":
+            up = lambda x: torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
+        else:
+            up = lambda x: torch.from_numpy(x).to(dev)
+        tensors = (up(q), up(k), up(v))
+        plans = [va.Plan(**d, in_dtype=dtype, out_dtype="fp32") for d in descs]
+        outs = [p.new_output(dev) for p in plans]
+        wss = [p.new_workspace(dev) for p in plans]
+        wall, attn = time_calls(plans, tensors, outs, wss, steps, warmup=1)
+        flops = [p.counts()["flops"] for p in plans]
+        T = plans[0].T
+        entry = {"name": name, "ms_per_step": wall * 1e3, "queries_per_s": T / wall,
+                 "tflops": sum(flops) / wall / 1e12, "pct_bf16_peak": 100 * sum(flops) / wall / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                 "attention": [{"form": ("g2f" if d.get("g2f") else f"sigma{d.get('sigma', 1)}"), "ms": a * 1e3,
+                                "tflops": f / a / 1e12, "frac_bf16_peak": f / a / 1e12 / MFMA_BF16_PEAK_TFLOPS}
+                               for d, a, f in zip(descs, attn, flops)]}
+        results.append(entry)
+        log(f"extra {name}: {wall * 1e3:.3f} ms/step, {entry['tflops']:.1f} TFLOP/s")
+        del tensors, outs, wss
+        torch.cuda.empty_cache()
+    return results
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -106,6 +172,7 @@ def main() -> int:
     ap.add_argument("--workload", default="sga6-800f", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=256, help="query rows in the oracle sample")
+    ap.add_argument("--no-extra", action="store_true", help="skip the other workloads")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (PMC scale calibration)")
     args = ap.parse_args()
@@ -180,6 +247,10 @@ def main() -> int:
 
     flops = counts["flops"]
     achieved = flops / t_attn / 1e12
+    if not args.no_cpu_baseline:  # keep the sampled rows of this run's output for the parity check
+        rows_all = sample_rows(desc["frames"], desc["grid_h"], desc["grid_w"], 5, count=4096, seed=1)
+        rows = rows_all[:: max(1, rows_all.size // args.cpu_rows)][: args.cpu_rows]
+        out_rows = out[:, torch.from_numpy(rows).to(dev)].double().cpu().numpy()
     traffic = measured_traffic(args.workload)
     gbytes = gather_bytes(desc, counts)
     result = {
@@ -210,18 +281,21 @@ def main() -> int:
         "device": torch.cuda.get_device_name(dev),
     }
 
+    if not args.no_extra:
+        del out, ws, qd, kd, vd
+        torch.cuda.empty_cache()
+        result["other_workloads"] = extra_workloads(dev, steps=3)
+
     if not args.no_cpu_baseline:
         import oracle
         from oracle import Desc
-        rows_all = sample_rows(desc["frames"], desc["grid_h"], desc["grid_w"], 5, count=4096, seed=1)
-        rows = rows_all[:: max(1, rows_all.size // args.cpu_rows)][: args.cpu_rows]
         odesc = Desc(**desc)
         cores = host_threads()
         log(f"oracle on {rows.size} rows x {H} heads with {cores} threads")
         c0 = time.perf_counter()
         ref = oracle.attention(q, k, v, odesc, rows=rows, workers=cores)
         c_s = time.perf_counter() - c0
-        got = out[:, torch.from_numpy(rows).to(dev)].double().cpu().numpy()
+        got = out_rows
         diff = got - ref
         result["cpu_baseline"] = {
             "value": rows.size / c_s, "unit": "queries/s", "cores": cores, "kind": "oracle",
