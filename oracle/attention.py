@@ -15,7 +15,11 @@ Sources (the pages are web notes on the methods; cited by page title and section
               diagonal kept; dropped tokens approximated by a mean token).
   [Regime]    "RegimeVGGT: Layer-Wise Spatially Preserving Redundancy Removal ...", papernotes.org
               NeurIPS 2026 notes: 核心机制 (L = T + 5 tokens per frame), 关键设计 2 (a key that
-              stands for g tokens gets +log g on its logit).
+              stands for g tokens gets +log g on its logit), 关键设计 3 (the K/V sampling grid of
+              frame f is shifted by row (f div t) mod t and column f mod t; frame 0 and the
+              camera/register tokens stay at full density).
+  [AVGGT-abl] the AVGGT notes' ablation table (VGGT on RealEstate10K, row VGGT(G2M)) and 关键发现:
+              G2M replaces the K/V of a global layer by one mean token.
 
 Readings taken where the pages are silent (each one is a stated choice, listed in the design
 notes of the repository):
@@ -34,6 +38,18 @@ notes of the repository):
   R12 the same S for every head.
   R13 means are taken of the K/V given to the op (after any upstream position encoding).
   R14 layout [H][T][d], batch 1.
+  R19 phase-shifted grid ([Regime] 关键设计 3) for a window (s_h, s_w): the tile size t of the page
+      becomes s_h for rows and s_w for columns, so compressed frame f keeps the patches with
+      row % s_h == (f div s_w) mod s_h and column % s_w == f mod s_w.  For square windows
+      (sigma 4, 9) this is the page's formula with t = s_h = s_w; for every window the offsets
+      of s_h*s_w consecutive frames run through all s_h*s_w residues, so their kept sets
+      partition the grid.  Frame 0 (with the reference flag) and the specials stay dense.
+  R20 global mean scope: one mean K/V over the union of the dropped sets of all frames (the
+      literal "single mean" of [AVGGT-zh] 关键设计 3); COUNT adds ln(sum_f |D_f|).
+  R21 G2M ([AVGGT-abl]): the keys/values of every query are one token, the mean of K and of V
+      over all T tokens (specials included); the output of every query is that mean value.
+  R22 a frame whose dropped set is empty (possible under the phase shift on one-patch-wide
+      grids) contributes no mean term.
 
 Parity: these functions are pinned by tests against torch's scaled-dot-product attention on
 explicitly built key lists, closed-form counts, hand-enumerated index sets and exact identities.
@@ -68,12 +84,19 @@ class Desc:
     mean: bool = False         # per-frame mean K/V of the dropped patches
     mean_count: bool = False   # mean logit += ln|D_f| (else unit weight)
     g2f: bool = False          # Global-to-Frame: each frame attends only to itself
+    phase_shift: bool = False  # per-frame offset of the sampling grid (reading R19)
+    mean_global: bool = False  # one mean over all dropped patches instead of one per frame (R20)
+    g2m: bool = False          # K/V = one mean token over all tokens (R21)
 
     def __post_init__(self):
         if self.sigma not in SIGMA_WINDOWS:
             raise ValueError(f"sigma must be one of {sorted(SIGMA_WINDOWS)}, got {self.sigma}")
         if self.g2f and (self.sigma != 1 or self.diag or self.mean):
             raise ValueError("Global-to-Frame takes no subsampling, diagonal or mean term")
+        if self.g2m and (self.sigma != 1 or self.diag or self.mean or self.g2f):
+            raise ValueError("G2M takes no subsampling, diagonal, per-frame mean or G2F")
+        if self.mean_global and not self.mean:
+            raise ValueError("mean_global selects the scope of the mean term; it needs mean=True")
         if min(self.frames, self.grid_h, self.grid_w, self.heads, self.head_dim) < 1 or self.n_special < 0:
             raise ValueError("sizes must be positive")
 
@@ -116,24 +139,38 @@ def frame_is_dense(desc: Desc, f: int) -> bool:
     return desc.sigma == 1 or (desc.ref_dense and f == 0)
 
 
+def grid_phase(desc: Desc, f: int) -> tuple[int, int]:
+    """(row offset, column offset) of the sampling grid of frame f: (0, 0) without the phase
+    shift; with it, [Regime] 关键设计 3 read for an s_h x s_w window (reading R19)."""
+    if not desc.phase_shift:
+        return 0, 0
+    s_h, s_w = desc.window
+    return (f // s_w) % s_h, f % s_w
+
+
 def kept_mask(desc: Desc) -> np.ndarray:
     """Boolean [T]: token t is in S.
 
     Token t = f*L + j; slot j < n_special is a camera/register token, always kept ([AVGGT-zh]
     关键设计 2, [AVGGT-de] 2.B).  Patch slot j >= n_special is patch p = j - n_special at row
     p // gw, column p % gw; in a compressed frame it is kept iff it is the first (top-left) patch
-    of its s_h x s_w window, i.e. row % s_h == 0 and column % s_w == 0 (readings R3, R4)."""
+    of its s_h x s_w window, i.e. row % s_h == 0 and column % s_w == 0 (readings R3, R4); with
+    the phase shift the windows start at the frame's offsets instead (R19).  G2M keeps no
+    token (R21)."""
     s_h, s_w = desc.window
     keep = np.zeros(desc.T, dtype=bool)
+    if desc.g2m:
+        return keep
     for f in range(desc.frames):
         base = f * desc.L
         keep[base:base + desc.n_special] = True
         if frame_is_dense(desc, f):
             keep[base:base + desc.L] = True
             continue
+        ro, co = grid_phase(desc, f)
         for p in range(desc.P):
             r, c = divmod(p, desc.grid_w)
-            if r % s_h == 0 and c % s_w == 0:
+            if r % s_h == ro and c % s_w == co:
                 keep[base + desc.n_special + p] = True
     return keep
 
@@ -144,15 +181,16 @@ def index_set(desc: Desc) -> np.ndarray:
 
 
 def dropped_counts(desc: Desc) -> np.ndarray:
-    """|D_f| per frame: the patches of frame f that are not in S (0 for dense frames)."""
+    """|D_f| per frame: the tokens of frame f that are not in S -- its dropped patches (0 for
+    dense frames); under G2M every token of the frame feeds the one mean (R21)."""
     keep = kept_mask(desc).reshape(desc.frames, desc.L)
     return (~keep).sum(axis=1).astype(np.int64)
 
 
 def mean_frames(desc: Desc) -> np.ndarray:
-    """Frames that contribute a mean K/V term (reading R9): those with a nonempty dropped set,
-    in ascending order; empty unless the MEAN form is on."""
-    if not desc.mean or desc.g2f:
+    """Frames that contribute to a mean K/V term (readings R9, R22): those with a nonempty
+    dropped set, in ascending order; empty unless the MEAN form (or G2M) is on."""
+    if not (desc.mean or desc.g2m) or desc.g2f:
         return np.zeros(0, dtype=np.int64)
     return np.flatnonzero(dropped_counts(desc) > 0).astype(np.int64)
 
@@ -162,26 +200,35 @@ def counts(desc: Desc) -> dict:
     if desc.g2f:
         return {"n_kv": desc.L, "n_mean": 0, "n_diag": 0}
     keep = kept_mask(desc)
+    nm = int(mean_frames(desc).size)
+    if desc.mean_global or desc.g2m:
+        nm = min(nm, 1)
     return {
         "n_kv": int(keep.sum()),
-        "n_mean": int(mean_frames(desc).size),
+        "n_mean": nm,
         "n_diag": int((~keep).sum()) if desc.diag else 0,
     }
 
 
 def frame_means(k: np.ndarray, v: np.ndarray, desc: Desc):
-    """Per-frame mean key and value over the dropped patches ([AVGGT-zh] 关键设计 3 (iii);
-    readings R9, R11, R13).  Returns (kbar [H][M][d], vbar [H][M][d], frames [M], |D_f| [M])
-    in float64."""
+    """Mean keys and values over the dropped tokens ([AVGGT-zh] 关键设计 3 (iii); readings
+    R9, R11, R13): one per frame with a nonempty dropped set, or -- global scope (R20) and G2M
+    (R21) -- a single one over the union of those sets.  Returns (kbar [H][M][d], vbar [H][M][d],
+    frames [M] (the first contributing frame for a single mean), sizes [M]) in float64."""
     frames = mean_frames(desc)
     keep = kept_mask(desc)
     H, d = k.shape[0], k.shape[2]
-    kbar = np.zeros((H, frames.size, d))
-    vbar = np.zeros((H, frames.size, d))
-    sizes = np.zeros(frames.size, dtype=np.int64)
-    for m, f in enumerate(frames):
+    groups = []
+    for f in frames:
         tok = np.arange(f * desc.L, (f + 1) * desc.L)
-        dropped = tok[~keep[tok]]
+        groups.append(tok[~keep[tok]])
+    if (desc.mean_global or desc.g2m) and groups:
+        groups = [np.concatenate(groups)]
+        frames = frames[:1]
+    kbar = np.zeros((H, len(groups), d))
+    vbar = np.zeros((H, len(groups), d))
+    sizes = np.zeros(len(groups), dtype=np.int64)
+    for m, dropped in enumerate(groups):
         sizes[m] = dropped.size
         kbar[:, m, :] = as_f64(k[:, dropped, :]).mean(axis=1)
         vbar[:, m, :] = as_f64(v[:, dropped, :]).mean(axis=1)
@@ -199,9 +246,11 @@ def attention(q, k, v, desc: Desc, rows=None, workers: int = 1, chunk: int = 256
     token t_q, the logits are tau*<q, k_t> for t in S, plus
       - DIAG: tau*<q, k_{t_q}> with value v_{t_q}, only if t_q is not in S (R8);
       - MEAN: tau*<q, kbar_f> + beta_f with value vbar_f for every compressed frame f, beta_f = 0
-        (UNIT) or ln|D_f| (COUNT, [Regime] 关键设计 2) (R9, R10);
+        (UNIT) or ln|D_f| (COUNT, [Regime] 关键设计 2) (R9, R10); global scope: one such term
+        over the union of the dropped sets (R20);
     and the output is the softmax-weighted sum of the values under one joint normalisation.
     G2F form ([AVGGT-zh] 关键设计 1): the keys of a query are the L tokens of its own frame.
+    G2M form (R21): a softmax over one key, so every output row is the mean value.
     sigma = 1 gives S = every token: plain global attention."""
     H, T, d = q.shape
     if T != desc.T or H != desc.heads or d != desc.head_dim:
@@ -210,7 +259,12 @@ def attention(q, k, v, desc: Desc, rows=None, workers: int = 1, chunk: int = 256
     out = np.empty((H, rows.size, d))
     tau = desc.tau
 
-    if desc.g2f:
+    if desc.g2m:
+        vbar = frame_means(k, v, desc)[1]
+
+        def run_head(h):
+            out[h] = vbar[h, 0][None, :]
+    elif desc.g2f:
         frame_of = rows // desc.L
 
         def run_head(h):
@@ -271,19 +325,21 @@ def _joint_softmax(parts) -> np.ndarray:
 
 def kept_mask_by_sets(desc: Desc) -> np.ndarray:
     """S built a second way, as a union of sets: all specials, all tokens of dense frames, and
-    the grid points {(r, c): r in range(0, gh, s_h), c in range(0, gw, s_w)} of every other
-    frame."""
+    the grid points {(r, c): r in range(r0, gh, s_h), c in range(c0, gw, s_w)} of every other
+    frame, (r0, c0) = (0, 0) or the frame's phase offsets."""
     s_h, s_w = desc.window
     keep = np.zeros(desc.T, dtype=bool)
+    if desc.g2m:
+        return keep
     frames = np.arange(desc.frames)
     keep[(frames[:, None] * desc.L + np.arange(desc.n_special)[None, :]).ravel()] = True
     dense = [f for f in frames if frame_is_dense(desc, int(f))]
     for f in dense:
         keep[f * desc.L:(f + 1) * desc.L] = True
-    rr, cc = np.meshgrid(np.arange(0, desc.grid_h, s_h), np.arange(0, desc.grid_w, s_w), indexing="ij")
-    grid = desc.n_special + (rr * desc.grid_w + cc).ravel()
     for f in frames:
-        keep[f * desc.L + grid] = True
+        r0, c0 = ((f // s_w) % s_h, f % s_w) if desc.phase_shift else (0, 0)
+        rr, cc = np.meshgrid(np.arange(r0, desc.grid_h, s_h), np.arange(c0, desc.grid_w, s_w), indexing="ij")
+        keep[f * desc.L + desc.n_special + (rr * desc.grid_w + cc).ravel()] = True
     return keep
 
 
@@ -294,7 +350,8 @@ def attention_bruteforce(q, k, v, desc: Desc) -> np.ndarray:
     matrix A[f, t] = 1/|D_f| for t in D_f.  A token column is open for a query row if the token
     is in S, or (DIAG) it is the row's own token and that token is not in S; under G2F a token
     column is open iff it lies in the row's frame.  A mean column is open when MEAN is on and
-    |D_f| > 0, with bias ln|D_f| under COUNT.  Meant for T up to a few thousand."""
+    |D_f| > 0, with bias ln|D_f| under COUNT.  Global mean scope and G2M use one mean column
+    whose row of A averages every token outside S.  Meant for T up to a few thousand."""
     H, T, d = q.shape
     q64, k64, v64 = as_f64(q), as_f64(k), as_f64(v)
     N, L = desc.frames, desc.L
@@ -312,12 +369,15 @@ def attention_bruteforce(q, k, v, desc: Desc) -> np.ndarray:
             open_tok[own[~keep], own[~keep]] = True
         dropped = ~keep
         A = np.zeros((N, T))
-        A[frame[dropped], np.flatnonzero(dropped)] = 1.0
+        if desc.mean_global or desc.g2m:
+            A[0, np.flatnonzero(dropped)] = 1.0
+        else:
+            A[frame[dropped], np.flatnonzero(dropped)] = 1.0
         size = A.sum(axis=1)
         with np.errstate(divide="ignore", invalid="ignore"):
             A = np.where(size[:, None] > 0, A / np.maximum(size, 1)[:, None], 0.0)
             bias = np.log(np.maximum(size, 1)) if desc.mean_count else np.zeros(N)
-        open_mean = np.broadcast_to((size > 0) & desc.mean, (T, N)).copy()
+        open_mean = np.broadcast_to((size > 0) & (desc.mean or desc.g2m), (T, N)).copy()
     mask = np.concatenate([open_tok, open_mean], axis=1)
     out = np.empty((H, T, d))
     for h in range(H):

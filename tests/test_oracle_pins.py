@@ -8,7 +8,12 @@ Each check ties the oracle to a fact the pages fix or to an independent route:
   * exact identities: a COUNT-weighted mean equals |D_f| copies of the mean token (RegimeVGGT
     notes, 关键设计 2, the log g bias); identical dropped rows make enhanced SGA collapse to dense
     attention; shift invariance in K; linearity in V; V = 1 gives 1;
-  * the oracle's own brute-force (full-mask) formulation, on small and odd grids.
+  * the oracle's own brute-force (full-mask) formulation, on small and odd grids;
+  * for the phase-shifted grid (RegimeVGGT notes, 关键设计 3): a hand-enumerated index set, the
+    page's offset formula for square windows, and the coverage the page states (consecutive
+    frames' grids together cover every patch);
+  * for the global mean scope and G2M: explicit key lists through torch SDPA, and the collapse
+    identity (identical keys give uniform weights, so attention returns the mean value).
 """
 import math
 import os
@@ -239,6 +244,10 @@ FORMS = [
     dict(sigma=9, diag=True, mean=True, ref_dense=False),
     dict(sigma=6, diag=True),
     dict(sigma=9, mean=True, mean_count=True, ref_dense=False),
+    dict(sigma=6, diag=True, mean=True, mean_count=True, phase_shift=True),
+    dict(sigma=4, diag=True, mean=True, mean_global=True),
+    dict(sigma=9, mean=True, mean_count=True, mean_global=True, phase_shift=True, ref_dense=False),
+    dict(g2m=True),
 ]
 
 
@@ -298,6 +307,159 @@ def test_invalid_descriptors_rejected():
         Desc(frames=2, grid_h=4, grid_w=4, heads=1, sigma=4, g2f=True)
     with pytest.raises(ValueError):
         Desc(frames=2, grid_h=4, grid_w=4, heads=1, g2f=True, mean=True)
+    with pytest.raises(ValueError):
+        Desc(frames=2, grid_h=4, grid_w=4, heads=1, sigma=4, g2m=True)
+    with pytest.raises(ValueError):
+        Desc(frames=2, grid_h=4, grid_w=4, heads=1, g2m=True, diag=True)
+    with pytest.raises(ValueError):
+        Desc(frames=2, grid_h=4, grid_w=4, heads=1, sigma=4, mean_global=True)
+
+
+# ------------------------------------------------------------------------------------------
+# Phase-shifted sampling grid (RegimeVGGT notes, 关键设计 3)
+# ------------------------------------------------------------------------------------------
+
+PHASE_DESC = dict(frames=7, grid_h=5, grid_w=7, heads=2, sigma=6, ref_dense=True, phase_shift=True)
+
+
+def phase_S():
+    return load_golden("index_set_7f_5x7_sigma6_phase.txt")
+
+
+def test_phase_shift_index_set_hand_enumerated():
+    d = Desc(**PHASE_DESC)
+    assert np.array_equal(oracle.index_set(d), phase_S())
+    assert np.array_equal(np.flatnonzero(oracle.kept_mask_by_sets(d)), phase_S())
+    assert list(oracle.dropped_counts(d)) == [0, 29, 29, 29, 31, 31, 26]
+    c = oracle.counts(Desc(**PHASE_DESC, diag=True, mean=True))
+    assert (c["n_kv"], c["n_mean"], c["n_diag"]) == (105, 6, 175)
+
+
+@pytest.mark.parametrize("sigma,t", [(4, 2), (9, 3)])
+def test_phase_shift_square_windows_follow_the_page_formula(sigma, t):
+    """Square t x t windows: frame f's grid starts at row (f div t) mod t, column f mod t."""
+    d = Desc(frames=20, grid_h=9, grid_w=9, heads=1, sigma=sigma, ref_dense=False, phase_shift=True)
+    keep = oracle.kept_mask(d).reshape(d.frames, d.L)[:, d.n_special:].reshape(d.frames, 9, 9)
+    for f in range(d.frames):
+        rows, cols = np.nonzero(keep[f])
+        assert set((rows % t).tolist()) == {(f // t) % t} and set((cols % t).tolist()) == {f % t}
+        assert rows.min() == (f // t) % t and cols.min() == f % t
+        assert rows.size == len(range((f // t) % t, 9, t)) * len(range(f % t, 9, t))
+
+
+@pytest.mark.parametrize("sigma", [2, 4, 6, 9])
+@pytest.mark.parametrize("geom", [(5, 7), (37, 37), (4, 4), (1, 5), (6, 1)])
+def test_phase_shift_consecutive_frames_cover_the_grid(sigma, geom):
+    """The page shifts the grid so that the union over frames covers the whole space: here any
+    s_h*s_w consecutive compressed frames keep every patch position exactly once."""
+    gh, gw = geom
+    s_h, s_w = oracle.SIGMA_WINDOWS[sigma]
+    n = s_h * s_w
+    for start in (0, 1, 5):
+        d = Desc(frames=start + n, grid_h=gh, grid_w=gw, heads=1, n_special=2, sigma=sigma,
+                 ref_dense=False, phase_shift=True)
+        keep = oracle.kept_mask(d).reshape(d.frames, d.L)[start:, d.n_special:]
+        assert np.array_equal(keep.sum(axis=0), np.ones(gh * gw, dtype=np.int64))
+
+
+def test_phase_shift_size_at_800_frames():
+    # 37 x 37 grid, 2 x 3 windows: phase (row, col) keeps 19|18 rows x 13|12|12 columns; one
+    # period of 6 phases keeps 247+228+228+234+216+216 = 1369 = every patch once.  Frames
+    # 1..798 are 133 full periods and frame 799 has phase 1 (228 patches).
+    expect = 800 * 5 + 1369 + 133 * 1369 + 228
+    assert expect == 187_674
+    d = Desc(frames=800, grid_h=37, grid_w=37, heads=1, sigma=6, phase_shift=True)
+    assert oracle.counts(d)["n_kv"] == expect
+
+
+def test_phase_shift_sga_is_attention_over_hand_set():
+    d = Desc(**PHASE_DESC)
+    q, k, v = inputs(d, seed=21)
+    S = phase_S()
+    ref = sdpa(f64(q), f64(k)[:, S], f64(v)[:, S])
+    np.testing.assert_allclose(oracle.attention(q, k, v, d), ref, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("weight", ["unit", "count"])
+def test_phase_shift_means_with_unequal_dropped_sets(weight):
+    """Per-frame means over dropped sets of different sizes (29, 31, 26 patches): COUNT equals
+    |D_f| copies of each frame's mean token."""
+    d = Desc(**PHASE_DESC, mean=True, mean_count=(weight == "count"))
+    q, k, v = inputs(d, seed=22)
+    qf, kf, vf = f64(q), f64(k), f64(v)
+    S = phase_S()
+    Sset = set(S.tolist())
+    ks, vs = [kf[:, S]], [vf[:, S]]
+    for f in range(1, d.frames):
+        D = np.asarray([t for t in range(f * 40 + 5, (f + 1) * 40) if t not in Sset])
+        assert D.size == [29, 29, 29, 31, 31, 26][f - 1]
+        n = D.size if weight == "count" else 1
+        ks.append(np.repeat(kf[:, D].mean(axis=1, keepdims=True), n, axis=1))
+        vs.append(np.repeat(vf[:, D].mean(axis=1, keepdims=True), n, axis=1))
+    ref = sdpa(qf, np.concatenate(ks, axis=1), np.concatenate(vs, axis=1))
+    np.testing.assert_allclose(oracle.attention(q, k, v, d), ref, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("flags", [dict(diag=True, mean=True), dict(diag=True, mean=True, mean_count=True),
+                                   dict(mean=True, mean_global=True, mean_count=True)])
+def test_phase_shift_one_wide_grid_with_empty_dropped_sets(flags):
+    """A 6 x 1 grid with 1 x 2 windows: even frames keep their whole column, odd frames keep
+    nothing, so only odd frames have a mean term (reading R22)."""
+    d = Desc(frames=5, grid_h=6, grid_w=1, heads=2, sigma=2, ref_dense=False, phase_shift=True, **flags)
+    assert list(oracle.dropped_counts(d)) == [0, 6, 0, 6, 0]
+    c = oracle.counts(d)
+    assert c["n_kv"] == 5 * 5 + 3 * 6
+    assert c["n_mean"] == (1 if d.mean_global else 2)
+    q, k, v = inputs(d, seed=23)
+    np.testing.assert_allclose(oracle.attention(q, k, v, d), oracle.attention_bruteforce(q, k, v, d),
+                               rtol=0, atol=1e-12)
+
+
+# ------------------------------------------------------------------------------------------
+# Global mean scope and G2M
+# ------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("weight", ["unit", "count"])
+def test_global_mean_is_one_token_over_all_dropped(weight):
+    """One mean over D_1 and D_2 together (52 patches): UNIT adds one token, COUNT adds 52
+    copies of it."""
+    d = Desc(**GOLD_DESC, mean=True, mean_global=True, mean_count=(weight == "count"))
+    q, k, v = inputs(d, seed=24)
+    qf, kf, vf = f64(q), f64(k), f64(v)
+    S = hand_S()
+    D = np.concatenate([hand_dropped(1), hand_dropped(2)])
+    n = D.size if weight == "count" else 1
+    keys = np.concatenate([kf[:, S], np.repeat(kf[:, D].mean(axis=1, keepdims=True), n, axis=1)], axis=1)
+    vals = np.concatenate([vf[:, S], np.repeat(vf[:, D].mean(axis=1, keepdims=True), n, axis=1)], axis=1)
+    np.testing.assert_allclose(oracle.attention(q, k, v, d), sdpa(qf, keys, vals), rtol=0, atol=1e-12)
+    assert oracle.counts(d)["n_mean"] == 1
+
+
+@pytest.mark.parametrize("phase", [False, True])
+def test_collapse_identity_global_mean(phase):
+    """If every dropped K/V row of every frame is the same row, the COUNT-weighted global mean
+    stands in for exactly those rows: SGA + global mean equals dense attention."""
+    d = Desc(frames=4, grid_h=6, grid_w=7, heads=2, sigma=6, mean=True, mean_global=True, mean_count=True,
+             phase_shift=phase)
+    q, k, v = inputs(d, dtype="fp32", seed=25)
+    drop = np.flatnonzero(~oracle.kept_mask_by_sets(d))
+    rng = np.random.default_rng(2)
+    k[:, drop] = rng.standard_normal((d.heads, 1, d.head_dim)).astype(np.float32)
+    v[:, drop] = rng.standard_normal((d.heads, 1, d.head_dim)).astype(np.float32)
+    np.testing.assert_allclose(oracle.attention(q, k, v, d), sdpa(f64(q), f64(k), f64(v)), rtol=0, atol=1e-12)
+
+
+def test_g2m_equals_attention_over_identical_keys():
+    """With every key equal, attention weights are uniform and the output of every query is
+    the mean value over all tokens -- which is what G2M computes for any keys."""
+    d = Desc(frames=3, grid_h=4, grid_w=5, heads=2, g2m=True)
+    q, k, v = inputs(d, dtype="fp32", seed=26)
+    out = oracle.attention(q, k, v, d)
+    k_same = np.broadcast_to(f64(k)[:, :1], k.shape)
+    np.testing.assert_allclose(out, sdpa(f64(q), k_same, f64(v)), rtol=0, atol=1e-12)
+    c = oracle.counts(d)
+    assert (c["n_kv"], c["n_mean"], c["n_diag"]) == (0, 1, 0)
+    assert list(oracle.dropped_counts(d)) == [d.L] * d.frames
 
 
 # ------------------------------------------------------------------------------------------
