@@ -15,7 +15,13 @@
  *                Spatially Preserving Redundancy Removal ..." (papernotes.org NeurIPS 2026
  *                notes, 关键设计 2);
  *   G2F          Global-to-Frame: each frame attends only to its own L tokens (AVGGT notes,
- *                关键设计 1).
+ *                关键设计 1);
+ *   G2M          Global-to-Mean: K/V of every query is one token, the mean of K and of V over
+ *                all T tokens (AVGGT notes, ablation table, row VGGT(G2M)), so every output row
+ *                is that mean value.
+ * Two options refine SGA: a phase-shifted sampling grid (RegimeVGGT notes, 关键设计 3: the grid
+ * of frame f is offset per frame so that consecutive frames together cover every patch) and a
+ * global scope for the mean term (one mean over every dropped patch of every frame).
  *
  * Conventions shared by every entry point
  *   - Tensors q, k, v, out are dense row-major [H][T][d], T = N*L, batch 1.  Within a frame
@@ -63,11 +69,22 @@ enum {
   VGGT_ATTN_DIAG = 1u << 2,       /* diagonal self term for queries whose token is not in S    */
   VGGT_ATTN_MEAN = 1u << 3,       /* one mean K/V per compressed frame, over its dropped patches */
   VGGT_ATTN_MEAN_COUNT = 1u << 4, /* mean logit += ln|D_f|, else the mean is one plain token    */
-  VGGT_ATTN_PRESCALE_Q = 1u << 5  /* bf16 path only: scale Q by tau*log2(e) once and round it to
+  VGGT_ATTN_PRESCALE_Q = 1u << 5, /* bf16 path only: scale Q by tau*log2(e) once and round it to
                                      bf16, saving one multiply per score (about 8% faster).  Every
                                      logit of a row then carries a coherent relative error of up to
                                      2^-9; without the flag Q is used exactly as given.  Ignored for
                                      fp32 inputs.                                                  */
+  VGGT_ATTN_PHASE_SHIFT = 1u << 6, /* SGA grid of frame f offset by row (f div s_w) mod s_h and
+                                     column f mod s_w (RegimeVGGT notes, 关键设计 3, whose t x t
+                                     formula this is for square windows): frame f keeps patch
+                                     (r, c) iff r % s_h and c % s_w equal those offsets.  Frame 0
+                                     (with REF_DENSE) and the specials stay dense.  |D_f| then
+                                     depends on f; no effect when sigma == 1.                     */
+  VGGT_ATTN_MEAN_GLOBAL = 1u << 7, /* with MEAN: one mean K/V over the union of all frames'
+                                     dropped patches instead of one per frame; MEAN_COUNT then adds
+                                     ln(sum_f |D_f|).  Requires MEAN.                              */
+  VGGT_ATTN_G2M = 1u << 8          /* Global-to-Mean (see above); needs sigma == 1 and none of
+                                     G2F, DIAG, MEAN, MEAN_GLOBAL, PHASE_SHIFT.                     */
 };
 
 typedef struct vggt_attn_plan_s vggt_attn_plan_t;
@@ -83,6 +100,8 @@ typedef struct {
   int64_t off_index;         /* int32[|S|]: S as ascending global token ids                  */
   int64_t off_dcount;        /* int32[N]: |D_f| per frame (0 for dense frames)               */
   int64_t off_means;         /* [H][M][2][d] input dtype: mean key, mean value               */
+  int64_t off_partial;       /* float [H][F][2][d]: per-frame sums of a global mean (F frames
+                                contribute; MEAN_GLOBAL and G2M only, else empty)             */
   int64_t off_kpack;         /* [H][segments*segment_rows][d] input dtype                    */
   int64_t off_vpack;         /* bf16: [H][rows/64][d][64] key-minor tiles (see below);
                                 fp32: [H][rows][d]                                           */
@@ -90,12 +109,18 @@ typedef struct {
 } vggt_attn_layout_t;
 
 /* Build a plan (host only; no device call is made, so it works without a GPU).
- * Operation: AVGGT notes 关键设计 1-3 as summarised at the top of this header.
+ * Operation: AVGGT notes 关键设计 1-3 and RegimeVGGT notes 关键设计 3 as summarised at the top
+ * of this header.
  *   frames >= 1, grid_h >= 1, grid_w >= 1, 0 <= n_special, heads >= 1;
  *   head_dim must be 64 (else EUNSUPPORTED);
- *   sigma in {1, 2, 4, 6, 9} (else EINVAL); sigma = 1 is dense attention (DIAG/MEAN then have
- *     no effect: no token is dropped);
- *   G2F requires sigma == 1 and neither DIAG nor MEAN (EINVAL);
+ *   sigma in {1, 2, 4, 6, 9} (else EINVAL); sigma = 1 is dense attention (DIAG/MEAN/PHASE_SHIFT
+ *     then have no effect: no token is dropped);
+ *   G2F requires sigma == 1 and none of DIAG, MEAN, MEAN_GLOBAL, PHASE_SHIFT, G2M (EINVAL);
+ *   G2M requires sigma == 1 and none of G2F, DIAG, MEAN, MEAN_GLOBAL, PHASE_SHIFT (EINVAL);
+ *   MEAN_GLOBAL requires MEAN (EINVAL);
+ *   a mean key exists for each frame whose dropped set is nonempty (one in all under
+ *     MEAN_GLOBAL and G2M); with PHASE_SHIFT a one-patch-wide grid can leave some frames'
+ *     dropped sets empty;
  *   (in_dtype, out_dtype) in {(BF16, FP32), (BF16, BF16), (FP32, FP32)} (EINVAL);
  *   T = frames*L must not exceed 8,000,000 and heads 4096 (EINVAL).
  * On success *out owns a plan to be released with vggt_attn_plan_destroy(). */
@@ -109,10 +134,10 @@ void vggt_attn_plan_destroy(vggt_attn_plan_t* plan);
 /* Workspace size in bytes for vggt_attn_forward / vggt_attn_pack (0 if plan is NULL). */
 size_t vggt_attn_workspace_bytes(const vggt_attn_plan_t* plan);
 
-/* Sizes of the call: n_kv = |S| (L under G2F), n_mean = M (number of mean keys), n_diag =
- * number of queries with a diagonal term, flops = algorithmic FLOPs of one forward:
- * 4*d*H*(T*(|S|+M) + n_diag) for the global forms, 4*d*H*N*L^2 for G2F (QK^T and PV
- * multiply-adds of attended keys only).  Any output pointer may be NULL. */
+/* Sizes of the call: n_kv = |S| (L under G2F, 0 under G2M), n_mean = M (number of mean keys),
+ * n_diag = number of queries with a diagonal term, flops = algorithmic FLOPs of one forward:
+ * 4*d*H*(T*(|S|+M) + n_diag) for the global forms (G2M: |S| = 0, M = 1), 4*d*H*N*L^2 for G2F
+ * (QK^T and PV multiply-adds of attended keys only).  Any output pointer may be NULL. */
 int vggt_attn_counts(const vggt_attn_plan_t* plan, int64_t* n_kv, int64_t* n_mean,
                      int64_t* n_diag, double* flops);
 
@@ -126,10 +151,12 @@ int vggt_attn_forward(const vggt_attn_plan_t* plan, const void* q, const void* k
                       void* out, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Gather/pack stage (AVGGT notes 关键设计 2 and 3): writes S (ascending token ids) and |D_f|
- * into the workspace, the per-frame mean key/value of the dropped patches (float32 sums
- * divided by |D_f|, rounded to the input dtype), and the packed keys and values: rows
- * [0,|S|) are exact copies of K/V rows of S, rows [|S|, |S|+M) the means, padding rows zero.
- * Under G2F (and sigma = 1) it packs every token, frame by frame.  Reads k and v only. */
+ * into the workspace, the mean keys/values (float32 sums divided by the number of tokens they
+ * stand for, rounded to the input dtype: per frame over its dropped patches, or once over all
+ * dropped patches with MEAN_GLOBAL, or once over all T tokens with G2M) and their logit
+ * biases, and the packed keys and values: rows [0,|S|) are exact copies of K/V rows of S, rows
+ * [|S|, |S|+M) the means, padding rows zero.  Under G2F (and sigma = 1) it packs every token,
+ * frame by frame.  |D_f| is L for every frame under G2M.  Reads k and v only. */
 int vggt_attn_pack(const vggt_attn_plan_t* plan, const void* k, const void* v, void* workspace,
                    size_t workspace_bytes, void* stream);
 

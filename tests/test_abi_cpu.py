@@ -55,13 +55,21 @@ CONFIGS = [
     Desc(3, 5, 7, 2, sigma=2, mean=True, mean_count=True),
     Desc(3, 1, 1, 2, sigma=9, diag=True, mean=True),  # every window is a single patch: nothing dropped
     Desc(2, 2, 1, 1, sigma=2, diag=True, mean=True),  # one column: (1,2) windows keep everything
+    Desc(7, 5, 7, 2, sigma=6, diag=True, mean=True, mean_count=True, phase_shift=True),
+    Desc(800, 37, 37, 16, sigma=6, diag=True, mean=True, phase_shift=True),
+    Desc(200, 37, 37, 16, sigma=9, diag=True, mean=True, mean_global=True, phase_shift=True, ref_dense=False),
+    Desc(100, 37, 37, 16, sigma=4, mean=True, mean_global=True, mean_count=True),
+    Desc(5, 6, 1, 2, sigma=2, diag=True, mean=True, phase_shift=True, ref_dense=False),  # empty dropped sets
+    Desc(32, 37, 37, 16, g2m=True),
 ]
 
 
-@pytest.mark.parametrize("desc", CONFIGS, ids=lambda d: f"{d.frames}x{d.grid_h}x{d.grid_w}-s{d.sigma}-g2f{int(d.g2f)}")
+@pytest.mark.parametrize("desc", CONFIGS, ids=lambda d: f"{d.frames}x{d.grid_h}x{d.grid_w}-s{d.sigma}-g2f{int(d.g2f)}"
+                         f"-ph{int(d.phase_shift)}-mg{int(d.mean_global)}-g2m{int(d.g2m)}")
 def test_plan_counts_match_oracle(va, desc):
     p = va.Plan(desc.frames, desc.grid_h, desc.grid_w, desc.heads, sigma=desc.sigma, ref_dense=desc.ref_dense,
-                diag=desc.diag, mean=desc.mean, mean_count=desc.mean_count, g2f=desc.g2f)
+                diag=desc.diag, mean=desc.mean, mean_count=desc.mean_count, g2f=desc.g2f,
+                phase_shift=desc.phase_shift, mean_global=desc.mean_global, g2m=desc.g2m)
     c = p.counts()
     o = oracle.counts(desc)
     assert (c["n_kv"], c["n_mean"], c["n_diag"]) == (o["n_kv"], o["n_mean"], o["n_diag"])
@@ -73,7 +81,7 @@ def test_plan_counts_match_oracle(va, desc):
     assert c["flops"] == pytest.approx(flops, rel=1e-12)
     lay = p.layout()
     assert lay["segment_rows"] % 64 == 0 and lay["segment_rows"] >= lay["keys_per_segment"]
-    for key in ("off_index", "off_dcount", "off_means", "off_kpack", "off_vpack", "total_bytes"):
+    for key in ("off_index", "off_dcount", "off_means", "off_partial", "off_kpack", "off_vpack", "total_bytes"):
         assert lay[key] % 256 == 0
     assert lay["total_bytes"] == p.workspace_bytes
 
@@ -94,8 +102,13 @@ def test_config5_sizes(va):
     (dict(g2f=True, sigma=4), "EINVAL"),
     (dict(g2f=True, mean=True), "EINVAL"),
     (dict(in_dtype="fp32", out_dtype="bf16"), "EINVAL"),
-    (dict(flags=1 << 7), "EINVAL"),
-    (dict(flags=1 << 6), "EINVAL"),
+    (dict(flags=1 << 9), "EINVAL"),
+    (dict(flags=1 << 12), "EINVAL"),
+    (dict(g2m=True, sigma=4), "EINVAL"),
+    (dict(g2m=True, diag=True), "EINVAL"),
+    (dict(g2m=True, g2f=True), "EINVAL"),
+    (dict(g2f=True, phase_shift=True), "EINVAL"),
+    (dict(sigma=4, mean_global=True), "EINVAL"),  # MEAN_GLOBAL without MEAN
     (dict(frames=0), "EINVAL"),
     (dict(heads=0), "EINVAL"),
     (dict(frames=6000, grid_h=37, grid_w=37), "EINVAL"),  # 8.2M tokens > limit

@@ -2,9 +2,11 @@
 (pack + attend through the C ABI), on 4096 seeded query rows per workload (all heads), which
 the oracle computes one by one; plus the bit-exact index set and |D_f| at full size.
 
-Workloads: dense 32 frames; SGA sigma 4 at 100 frames (UNIT and COUNT means); G2F and SGA
-sigma 9 on the same 200-frame tensors; SGA sigma 6 at 800 frames.  All use 37x37 patches + 5
-special tokens per frame, 16 heads, d = 64, bf16 inputs and fp32 output."""
+Workloads: dense 32 frames (and G2M on the same tensors); SGA sigma 4 at 100 frames (UNIT and
+COUNT means); G2F, SGA sigma 9, and sigma 9 with the phase-shifted grid and a global COUNT
+mean on the same 200-frame tensors; SGA sigma 6 at 800 frames, with and without the phase
+shift.  All use 37x37 patches + 5 special tokens per frame, 16 heads, d = 64, bf16 inputs and
+fp32 output."""
 import numpy as np
 import pytest
 
@@ -17,11 +19,15 @@ pytestmark = pytest.mark.gpu
 
 FULL = [
     ("dense-32f", Desc(32, 37, 37, 16, sigma=1)),
+    ("g2m-32f", Desc(32, 37, 37, 16, g2m=True)),
     ("sga4-100f", Desc(100, 37, 37, 16, sigma=4, diag=True, mean=True)),
     ("sga4-100f-count", Desc(100, 37, 37, 16, sigma=4, diag=True, mean=True, mean_count=True)),
     ("g2f-200f", Desc(200, 37, 37, 16, g2f=True)),
     ("sga9-200f", Desc(200, 37, 37, 16, sigma=9, diag=True, mean=True)),
+    ("sga9-200f-phase-global-count", Desc(200, 37, 37, 16, sigma=9, diag=True, mean=True, mean_count=True,
+                                          phase_shift=True, mean_global=True)),
     ("sga6-800f", Desc(800, 37, 37, 16, sigma=6, diag=True, mean=True)),
+    ("sga6-800f-phase", Desc(800, 37, 37, 16, sigma=6, diag=True, mean=True, phase_shift=True)),
 ]
 
 _cache = {}

@@ -1,8 +1,8 @@
 """GPU parity at sizes the oracle finishes in seconds: several key and query tiles, ragged
 tails, every form (dense, SGA sigma 2/4/6/9, enhanced SGA with UNIT and COUNT means, pi^3
-without a dense frame, G2F), both output types, plus the bit-exact index set and packed rows,
-V = 1, determinism, a NaN-poisoned workspace and the C ABI's error codes.  Every call goes
-through the C ABI of libvggt_attn.so."""
+without a dense frame, the phase-shifted grid, the global mean scope, G2F, G2M), both output
+types, plus the bit-exact index set and packed rows, V = 1, determinism, a NaN-poisoned
+workspace and the C ABI's error codes.  Every call goes through the C ABI of libvggt_attn.so."""
 import ctypes
 import zlib
 
@@ -28,7 +28,19 @@ CASES = [
     (Desc(3, 37, 37, 2, sigma=1), "dense-37x37"),
     (Desc(4, 37, 37, 2, g2f=True), "g2f-37x37"),
     (Desc(9, 37, 37, 1, sigma=9, diag=True, mean=True, mean_count=True), "sga9-enh-count-37x37"),
+    # phase-shifted grid (per-frame |D_f| and COUNT bias), global mean scope, G2M
+    (Desc(7, 5, 7, 2, sigma=6, diag=True, mean=True, mean_count=True, phase_shift=True), "sga6-phase-count-tiny"),
+    (Desc(8, 13, 11, 2, sigma=6, diag=True, mean=True, mean_count=True, phase_shift=True), "sga6-phase-count"),
+    (Desc(10, 37, 37, 1, sigma=9, diag=True, mean=True, mean_count=True, phase_shift=True, ref_dense=False),
+     "sga9-phase-pi3-37x37"),
+    (Desc(6, 13, 11, 2, sigma=4, diag=True, mean=True, mean_global=True), "sga4-global"),
+    (Desc(6, 13, 11, 2, sigma=4, diag=True, mean=True, mean_global=True, mean_count=True, phase_shift=True),
+     "sga4-global-count-phase"),
+    (Desc(5, 6, 1, 2, sigma=2, diag=True, mean=True, mean_count=True, phase_shift=True, ref_dense=False),
+     "sga2-phase-empty-sets"),
+    (Desc(4, 13, 11, 2, g2m=True), "g2m"),
 ]
+NEW = {c[1]: c for c in CASES[11:]}
 
 
 @pytest.fixture(scope="module")
@@ -73,6 +85,9 @@ FP32_CASES = [
     (Desc(3, 5, 7, 2, sigma=1), "fp32-dense"),
     (Desc(3, 9, 9, 2, g2f=True), "fp32-g2f"),
     (Desc(3, 6, 7, 2, sigma=9, diag=True, mean=True), "fp32-sga9"),
+    (Desc(7, 5, 7, 2, sigma=6, diag=True, mean=True, mean_count=True, phase_shift=True), "fp32-phase-count"),
+    (Desc(4, 8, 8, 2, sigma=4, diag=True, mean=True, mean_global=True, mean_count=True), "fp32-global-count"),
+    (Desc(3, 5, 7, 2, g2m=True), "fp32-g2m"),
 ]
 
 
@@ -100,7 +115,11 @@ def key_at(p):
     return half * 32 + (g * 4 + j if j < 4 else 16 + g * 4 + (j - 4))
 
 
-@pytest.mark.parametrize("desc,label", [CASES[3], CASES[5], CASES[6], CASES[7]], ids=["sga4", "sga9-pi3", "g2f", "sga4-37"])
+PACKED = [CASES[3], CASES[5], CASES[6], CASES[7], NEW["sga6-phase-count"], NEW["sga4-global-count-phase"],
+          NEW["sga2-phase-empty-sets"], NEW["g2m"]]
+
+
+@pytest.mark.parametrize("desc,label", PACKED, ids=[c[1] for c in PACKED])
 def test_packed_rows(lib, desc, label):
     """Rows of S are bit-exact copies; the means are within one bf16 step of the fp64 means;
     padding is zero; values sit in the key-minor tile order."""
@@ -138,7 +157,10 @@ def test_packed_rows(lib, desc, label):
     assert not kp[:, nS + M:].any() and not vrows[:, nS + M:].any()
 
 
-@pytest.mark.parametrize("desc,label", [CASES[4], CASES[5], CASES[6]], ids=["sga6-count", "sga9-pi3", "g2f"])
+VONES = [CASES[4], CASES[5], CASES[6], NEW["sga6-phase-count"], NEW["sga4-global-count-phase"], NEW["g2m"]]
+
+
+@pytest.mark.parametrize("desc,label", VONES, ids=[c[1] for c in VONES])
 def test_v_ones_gives_ones(lib, desc, label):
     q, k, _ = inputs_for(desc, "bf16", seed=5)
     v = np.full(q.shape, 0x3F80, dtype=np.uint16)  # bf16 1.0
@@ -237,7 +259,10 @@ def test_running_max_catch_up(lib, desc, label):
     assert_close(got, ref, fp32=False, label=label + "/spike")
 
 
-@pytest.mark.parametrize("desc,label", [CASES[i] for i in (2, 4, 5, 7, 9)], ids=[CASES[i][1] for i in (2, 4, 5, 7, 9)])
+PRESCALED = [CASES[i] for i in (2, 4, 5, 7, 9)] + [NEW["sga6-phase-count"], NEW["sga4-global-count-phase"]]
+
+
+@pytest.mark.parametrize("desc,label", PRESCALED, ids=[c[1] for c in PRESCALED])
 def test_parity_prescaled_q(lib, desc, label):
     """The opt-in PRESCALE_Q form (Q scaled by tau*log2(e) and rounded to bf16 once) on the
     seeded workload inputs."""

@@ -14,6 +14,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libvggt_att
 
 BF16, FP32 = 0, 1
 G2F, REF_DENSE, DIAG, MEAN, MEAN_COUNT, PRESCALE_Q = 1, 2, 4, 8, 16, 32
+PHASE_SHIFT, MEAN_GLOBAL, G2M = 64, 128, 256
 
 STATUS = {0: "OK", -1: "EINVAL", -2: "EUNSUPPORTED", -3: "ENOSPC", -4: "EALIGN", -5: "EALIAS", -6: "EHIP"}
 
@@ -32,7 +33,7 @@ class VggtAttnError(RuntimeError):
 class Layout(ctypes.Structure):
     _fields_ = [(name, ctypes.c_int64) for name in (
         "segments", "segment_rows", "keys_per_segment", "off_index", "off_dcount", "off_means",
-        "off_kpack", "off_vpack", "total_bytes")]
+        "off_partial", "off_kpack", "off_vpack", "total_bytes")]
 
     def as_dict(self) -> dict:
         return {name: int(getattr(self, name)) for name, _ in self._fields_}
@@ -107,11 +108,13 @@ class Plan:
                  n_special: int = 5, sigma: int = 1, ref_dense: bool = True, diag: bool = False,
                  mean: bool = False, mean_count: bool = False, g2f: bool = False,
                  in_dtype: str = "bf16", out_dtype: str = "fp32", prescale_q: bool = False,
+                 phase_shift: bool = False, mean_global: bool = False, g2m: bool = False,
                  flags: int | None = None):
         if flags is None:
             flags = ((G2F if g2f else 0) | (REF_DENSE if ref_dense else 0) | (DIAG if diag else 0) |
                      (MEAN if mean else 0) | (MEAN_COUNT if mean_count else 0) |
-                     (PRESCALE_Q if prescale_q else 0))
+                     (PRESCALE_Q if prescale_q else 0) | (PHASE_SHIFT if phase_shift else 0) |
+                     (MEAN_GLOBAL if mean_global else 0) | (G2M if g2m else 0))
         self._h = ctypes.c_void_p()
         self.frames, self.grid_h, self.grid_w, self.heads, self.head_dim = frames, grid_h, grid_w, heads, head_dim
         self.n_special, self.sigma, self.flags = n_special, sigma, flags
@@ -201,7 +204,7 @@ class Plan:
         """(S as int32 token ids, |D_f| per frame) copied from a packed workspace."""
         c = self.counts()
         g2f = bool(self.flags & G2F)
-        idx = np.zeros(0 if g2f else c["n_kv"], dtype=np.int32)
+        idx = np.zeros(0 if g2f else c["n_kv"], dtype=np.int32)  # n_kv is 0 under G2M
         dcount = np.zeros(self.frames, dtype=np.int32)
         i32p = ctypes.POINTER(ctypes.c_int32)
         _check(lib().vggt_attn_copy_index_set(

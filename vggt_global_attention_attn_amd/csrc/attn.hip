@@ -60,8 +60,11 @@ struct AttnArgs {
   int n_plain;     // keys before the mean keys
   int nktiles;     // ceil(nkeys / 64)
   int slow_from;   // first tile that holds a mean key or padding
-  float bias_s;    // fp32 path: added to the raw score q.k of a mean key (COUNT), else 0
-  float bias_log2; // bf16 path: the same bias in log2 units, ln|D_f| * log2(e)
+  // COUNT bias of mean key m: slot s = (m + mean_off) % mean_run indexes the mean frames of one
+  // run of grid phases (per-frame scope under the phase shift; otherwise one slot).
+  int mean_off, mean_run;
+  float mean_bias_s[kMaxPhases];     // raw-score units, ln(n)/tau (0 for UNIT weighting)
+  float mean_bias_log2[kMaxPhases];  // the same in log2 units, log2(n) (PRESCALE_Q path)
   float c_log2;    // tau * log2(e)
   int qtiles;      // query tiles per head
   int g2f;
@@ -69,6 +72,12 @@ struct AttnArgs {
   int diag;
   IndexGeom g;
 };
+
+// Logit bias of mean key m (0 <= m < M): it depends only on the grid phase of the frame the
+// key stands for, i.e. on the key's slot within a run of phases.
+__device__ __forceinline__ float mean_bias(const AttnArgs& a, const float (&tab)[kMaxPhases], int m) {
+  return a.mean_run > 1 ? pick(tab, (m + a.mean_off) % a.mean_run) : tab[0];
+}
 
 // This file is compiled with -fno-honor-nans (scores are never NaN; infinities are honoured),
 // so fmaxf lowers to plain v_max_f32 and chains of it fuse into v_max3_f32.
@@ -134,9 +143,7 @@ void attn_bf16_kernel(AttnArgs a) {
   const uint16_t* vseg = static_cast<const uint16_t*>(a.vpack) + seg_off;
 
   // Q as the B operand of S^T = K Q^T: lane (l16, grp) holds query l16 of its block and
-  // channels cc*32 + grp*8 .. +7 for cc = 0, 1.  Q is scaled once by c = tau*log2(e) and
-  // rounded back to bf16, so the matrix core yields scores directly in log2 units and the
-  // softmax exponent needs no per-score multiply.
+  // channels cc*32 + grp*8 .. +7 for cc = 0, 1.
   bf16x8_t qf[QB][2];
   float m_run[QB], l_run[QB];  // running max (log2 units) and lane-partial row sum
   f32x4_t o[QB][4];
@@ -240,13 +247,17 @@ void attn_bf16_kernel(AttnArgs a) {
   // Mean-key bias and padding mask, only for the last tiles of the segment.
   auto bias_mask = [&](int j, f32x4_t (&s)[QB][4]) {
     if (j < a.slow_from) return;
-    const float bias = PRESCALE_Q ? a.bias_log2 : a.bias_s;
 #pragma unroll
     for (int k4 = 0; k4 < 4; ++k4) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int key = j * kTile + k4 * 16 + grp * 4 + i;
-        const float add = key >= a.nkeys ? -INFINITY : (key >= a.n_plain ? bias : 0.f);
+        float bias = 0.f;
+        if (key >= a.n_plain) {
+          if constexpr (PRESCALE_Q) bias = mean_bias(a, a.mean_bias_log2, key - a.n_plain);
+          else bias = mean_bias(a, a.mean_bias_s, key - a.n_plain);
+        }
+        const float add = key >= a.nkeys ? -INFINITY : bias;
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) s[qb][k4][i] += add;
       }
@@ -495,7 +506,7 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
       for (int d = 0; d < kHeadDim; ++d) dot = fmaf(q[d], ks[kk][d], dot);
       const int key = j * kTile + kk;
       if (key >= a.nkeys) dot = -INFINITY;
-      else if (key >= a.n_plain) dot += a.bias_s;
+      else if (key >= a.n_plain) dot += mean_bias(a, a.mean_bias_s, key - a.n_plain);
       sc[kk] = dot;
       mx = fmaxf(mx, dot);
     }
@@ -542,10 +553,26 @@ hipError_t launch_attend(const vggt_attn_plan_s& p, const void* q, const void* k
   a.nktiles = int(p.segment_rows / kTile);
   a.slow_from = int(p.n_plain / kTile);
   const double tau = 1.0 / std::sqrt(double(p.head_dim));
-  // COUNT: logit += ln|D_f|  <=>  raw score q.k += ln|D_f| / tau.
-  a.bias_s = (p.mean_count && p.M > 0) ? float(std::log(double(p.dropped)) / tau) : 0.f;
+  // COUNT: logit += ln(n)  <=>  raw score q.k += ln(n) / tau, n = tokens behind the mean key.
+  // Per-frame means under the phase shift: the mean frames of one run of nphase frames are the
+  // phases with a nonempty dropped set, in phase order; mean key 0 is frame f0's slot.
+  a.mean_off = 0;
+  a.mean_run = 1;
+  const IndexGeom& g = p.geom;
+  const bool per_slot = p.M > 0 && !p.mean_global && !p.g2m && g.nphase > 1;
+  int slot_phase[kMaxPhases] = {0};
+  if (per_slot) {
+    a.mean_run = g.mprefix[g.nphase];
+    a.mean_off = g.mprefix[g.f0 % g.nphase];
+    for (int k = 0; k < g.nphase; ++k)
+      if (g.mprefix[k + 1] > g.mprefix[k]) slot_phase[g.mprefix[k]] = k;
+  }
+  for (int s = 0; s < kMaxPhases; ++s) {
+    const double b = p.mean_bias_s[per_slot ? slot_phase[s] : 0];
+    a.mean_bias_s[s] = float(b);
+    a.mean_bias_log2[s] = float(b * tau * 1.4426950408889634);
+  }
   a.c_log2 = float(tau * 1.4426950408889634);
-  a.bias_log2 = (p.mean_count && p.M > 0) ? float(std::log2(double(p.dropped))) : 0.f;
   a.g2f = p.g2f ? 1 : 0;
   a.diag = p.diag ? 1 : 0;
   a.g = p.geom;

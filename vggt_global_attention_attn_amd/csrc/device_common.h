@@ -1,5 +1,5 @@
-// Device-side helpers shared by the gfx950 kernels: vector types, bf16 conversions and the
-// closed-form description of the kept set S.
+// Helpers shared by the gfx950 kernels: vector types, bf16 conversions and the closed-form
+// description of the kept set S and of the mean frames (integer code, also callable on the host).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -22,41 +22,95 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return uint32_t(f32_to_bf16(lo)) | (uint32_t(f32_to_bf16(hi)) << 16);
 }
 
-// Is token t (global id) in S?  "AVGGT" notes, 关键设计 2: specials always; every token of a
-// dense frame; in a compressed frame the top-left patch of each s_h x s_w window.
-__device__ __forceinline__ bool token_kept(const IndexGeom& g, int64_t t) {
-  if (!g.subsampled) return true;
-  const int f = int(t / g.L);
-  const int j = int(t - int64_t(f) * g.L);
-  if (j < g.n_special || (g.ref_dense && f == 0)) return true;
-  const int p = j - g.n_special;
-  const int r = p / g.grid_w, c = p - (p / g.grid_w) * g.grid_w;
-  return (r % g.s_h) == 0 && (c % g.s_w) == 0;
+// t[i] for a run-time i, written as a chain of selects over compile-time indices: indexing an
+// array of the kernel-argument struct with a run-time value would make the compiler copy the
+// whole struct to scratch memory.
+template <typename V, int N>
+__host__ __device__ __forceinline__ V pick(const V (&t)[N], int i) {
+  V r = t[0];
+#pragma unroll
+  for (int j = 1; j < N; ++j) r = (i == j) ? t[j] : r;
+  return r;
 }
 
-// The i-th element of S in ascending order (0 <= i < |S|), in closed form.
-__device__ __forceinline__ int64_t token_of_kept_index(const IndexGeom& g, int64_t i) {
+// Largest k < n with prefix[k] <= x, for a nondecreasing prefix with prefix[0] <= x: the
+// number of j in [1, n) with prefix[j] <= x.
+template <int N>
+__host__ __device__ __forceinline__ int prefix_slot(const int (&prefix)[N], int n, int x) {
+  int k = 0;
+#pragma unroll
+  for (int j = 1; j < N; ++j) k += int(j < n) & int(prefix[j] <= x);
+  return k;
+}
+
+// Grid phase of frame f: f mod (s_h*s_w) with the phase-shifted grid, else 0.  Phase k has
+// row offset k / s_w and column offset k % s_w ("RegimeVGGT" notes, 关键设计 3).
+__host__ __device__ __forceinline__ int frame_phase(const IndexGeom& g, int64_t f) {
+  return g.nphase > 1 ? int(f % g.nphase) : 0;
+}
+
+// Is patch (r, c) of a compressed frame of phase k kept?  "AVGGT" notes, 关键设计 2: the first
+// patch of each s_h x s_w window, the windows starting at the phase's offsets.
+__host__ __device__ __forceinline__ bool patch_kept(const IndexGeom& g, int k, int r, int c) {
+  const int ro = k / g.s_w, co = k - ro * g.s_w;
+  return (r % g.s_h) == ro && (c % g.s_w) == co;
+}
+
+// Is token t (global id) in S?  Specials always; every token of a dense frame; in a
+// compressed frame the grid points of its phase.  Under G2M no token is.
+__host__ __device__ __forceinline__ bool token_kept(const IndexGeom& g, int64_t t) {
+  if (g.g2m) return false;
+  if (!g.subsampled) return true;
+  const int64_t f = t / g.L;
+  const int j = int(t - f * g.L);
+  if (j < g.n_special || (g.ref_dense && f == 0)) return true;
+  const int p = j - g.n_special;
+  const int r = p / g.grid_w, c = p - r * g.grid_w;
+  return patch_kept(g, frame_phase(g, f), r, c);
+}
+
+// |D_f|: the tokens of frame f that feed its mean (dropped patches; every token under G2M).
+__host__ __device__ __forceinline__ int frame_dropped(const IndexGeom& g, int64_t f) {
+  if (g.g2m) return g.L;
+  if (!g.subsampled || (g.ref_dense && f == 0)) return 0;
+  const int k = frame_phase(g, f);
+  return g.P - pick(g.rows_of, k / g.s_w) * pick(g.cols_of, k % g.s_w);
+}
+
+// The i-th element of S in ascending order (0 <= i < |S|), in closed form.  Compressed frames
+// are counted as if frame 0 were compressed too ("virtual" index); one run of nphase frames
+// holds cprefix[nphase] entries of S, and phase k starts at cprefix[k] within its run.
+__host__ __device__ __forceinline__ int64_t token_of_kept_index(const IndexGeom& g, int64_t i) {
   if (!g.subsampled) return i;
-  const int64_t per = g.n_special + g.kept;  // S entries of one compressed frame
-  int64_t f, j;
   if (g.ref_dense) {
     if (i < g.L) return i;
-    const int64_t r = i - g.L;
-    f = 1 + r / per;
-    j = r - (f - 1) * per;
-  } else {
-    f = i / per;
-    j = i - f * per;
+    i -= g.L;
   }
-  int64_t slot;
-  if (j < g.n_special) {
-    slot = j;
-  } else {
-    const int kp = int(j - g.n_special);
-    const int kr = kp / g.kw, kc = kp - (kp / g.kw) * g.kw;
-    slot = g.n_special + int64_t(kr) * g.s_h * g.grid_w + int64_t(kc) * g.s_w;
-  }
-  return f * g.L + slot;
+  const int period = pick(g.cprefix, g.nphase);
+  const int64_t v = i + int64_t(g.f0 / g.nphase) * period + pick(g.cprefix, g.f0 % g.nphase);
+  const int64_t run = v / period;
+  const int rem = int(v - run * period);
+  const int k = prefix_slot(g.cprefix, g.nphase, rem);
+  const int64_t f = run * g.nphase + k;
+  const int j = rem - pick(g.cprefix, k);
+  if (j < g.n_special) return f * g.L + j;
+  const int ro = k / g.s_w, co = k - ro * g.s_w;
+  const int nc = pick(g.cols_of, co);
+  const int kp = j - g.n_special;
+  const int kr = kp / nc, kc = kp - kr * nc;
+  return f * g.L + g.n_special + int64_t(ro + kr * g.s_h) * g.grid_w + (co + kc * g.s_w);
+}
+
+// Frame of the m-th frame that feeds a mean (0 <= m < number of such frames): the compressed
+// frames with a nonempty dropped set in ascending order (every frame under G2M).  One run of
+// nphase frames holds mprefix[nphase] of them.
+__host__ __device__ __forceinline__ int64_t mean_frame(const IndexGeom& g, int64_t m) {
+  if (g.g2m) return m;
+  const int per = pick(g.mprefix, g.nphase);
+  const int64_t v = m + int64_t(g.f0 / g.nphase) * per + pick(g.mprefix, g.f0 % g.nphase);
+  const int64_t run = v / per;
+  const int rem = int(v - run * per);
+  return run * g.nphase + prefix_slot(g.mprefix, g.nphase, rem);
 }
 
 }  // namespace vggt

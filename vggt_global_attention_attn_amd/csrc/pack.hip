@@ -1,18 +1,24 @@
 // Gather/pack stage of subsampled global attention on gfx950.
 //
 // "AVGGT: Rethinking Global Attention for Accelerating VGGT" (papernotes.org CVPR 2026 notes),
-// 关键设计 2: the keys and values of the global layer are restricted to S; 关键设计 3: one mean
-// key/value stands in for the dropped patches.  Both kernels are HBM-bound streaming passes.
+// 关键设计 2: the keys and values of the global layer are restricted to S; 关键设计 3: mean keys
+// and values stand in for the dropped patches; ablation table (G2M): one mean token replaces
+// all keys and values.  "RegimeVGGT ..." notes, 关键设计 3: per-frame phase of the grid.  All
+// kernels are HBM-bound streaming passes.
 //
-//   means_kernel  one work-group per (compressed frame, head): float32 sums of the frame's
-//                 dropped K and V rows (16-byte loads, 32 rows in flight per work-group),
-//                 divided by |D_f| and rounded to the input type.
-//   pack_kernel   one work-group per (64-row key tile, head): copies the K/V rows of S (and
-//                 the means, then zero padding) into packed tiles.  Keys stay row-major
-//                 [row][d]; for bf16 the values are written as [d][64] key-minor tiles in the
-//                 order the PV matrix-core step reads them, so the attention kernel loads
-//                 every operand with contiguous 16-byte reads.  Head 0 also exports S, and
-//                 work-group (0,0) exports |D_f|.
+//   means_kernel         one work-group per (frame feeding a mean, head): float32 sums of the
+//                        frame's dropped K and V rows (16-byte loads, 32 rows in flight per
+//                        work-group).  Per-frame scope: divided by |D_f| and rounded to the
+//                        input type.  Single mean (global scope, G2M): the float32 sums are
+//                        kept for means_reduce_kernel.
+//   means_reduce_kernel  one work-group per head: adds the per-frame sums in frame order,
+//                        divides by the number of tokens and rounds.
+//   pack_kernel          one work-group per (64-row key tile, head): copies the K/V rows of S
+//                        (and the means, then zero padding) into packed tiles.  Keys stay
+//                        row-major [row][d]; for bf16 the values are written as [d][64]
+//                        key-minor tiles in the order the PV matrix-core step reads them, so
+//                        the attention kernel loads every operand with contiguous 16-byte
+//                        reads.  Head 0 also exports S, and work-group (0,0) exports |D_f|.
 #include <hip/hip_runtime.h>
 
 #include "device_common.h"
@@ -24,10 +30,11 @@ namespace {
 struct MeansArgs {
   const void* k;
   const void* v;
-  void* means;  // [H][M][2][64]
+  void* means;     // [H][M][2][64] input type (per-frame scope)
+  float* partial;  // [H][F][2][64] float32 sums (single mean), else nullptr
   int64_t T;
-  int M;
-  int dropped;
+  int M;           // mean keys
+  int F;           // frames feeding a mean
   IndexGeom g;
 };
 
@@ -61,19 +68,24 @@ __global__ __launch_bounds__(256) void means_kernel(MeansArgs a) {
   constexpr int CPR = kHeadDim / CH;       // chunks per row
   constexpr int RG = 256 / CPR;            // rows in flight
   const int m = blockIdx.x, h = blockIdx.y;
-  const int f = a.g.ref_dense ? m + 1 : m;
+  const int64_t f = mean_frame(a.g, m);
+  const int k = frame_phase(a.g, f);
   const int tid = threadIdx.x, chunk = tid % CPR, rg = tid / CPR;
-  const size_t base = (size_t(h) * size_t(a.T) + size_t(f) * a.g.L + a.g.n_special) * kHeadDim + chunk * CH;
+  const size_t base = (size_t(h) * size_t(a.T) + size_t(f) * a.g.L) * kHeadDim + chunk * CH;
   const E* kb = static_cast<const E*>(a.k) + base;
   const E* vb = static_cast<const E*>(a.v) + base;
   float ks[CH], vs[CH];
 #pragma unroll
   for (int i = 0; i < CH; ++i) ks[i] = vs[i] = 0.f;
-  for (int p = rg; p < a.g.P; p += RG) {
-    const int r = p / a.g.grid_w, c = p - r * a.g.grid_w;
-    if ((r % a.g.s_h) == 0 && (c % a.g.s_w) == 0) continue;  // kept: not part of D_f
-    add_chunk<E>(ks, *reinterpret_cast<const uint4*>(kb + size_t(p) * kHeadDim));
-    add_chunk<E>(vs, *reinterpret_cast<const uint4*>(vb + size_t(p) * kHeadDim));
+  for (int j = rg; j < a.g.L; j += RG) {
+    if (!a.g.g2m) {
+      if (j < a.g.n_special) continue;  // specials are always kept
+      const int p = j - a.g.n_special;
+      const int r = p / a.g.grid_w, c = p - r * a.g.grid_w;
+      if (patch_kept(a.g, k, r, c)) continue;  // kept: not part of D_f
+    }
+    add_chunk<E>(ks, *reinterpret_cast<const uint4*>(kb + size_t(j) * kHeadDim));
+    add_chunk<E>(vs, *reinterpret_cast<const uint4*>(vb + size_t(j) * kHeadDim));
   }
   __shared__ float red[RG][2][kHeadDim];
 #pragma unroll
@@ -86,9 +98,29 @@ __global__ __launch_bounds__(256) void means_kernel(MeansArgs a) {
     const int which = tid / kHeadDim, ch = tid % kHeadDim;
     float s = 0.f;
     for (int r = 0; r < RG; ++r) s += red[r][which][ch];
-    E* dst = static_cast<E*>(a.means) + ((size_t(h) * a.M + m) * 2 + which) * kHeadDim + ch;
-    store_elem(dst, s / float(a.dropped));
+    if (a.partial) {
+      a.partial[((size_t(h) * a.F + m) * 2 + which) * kHeadDim + ch] = s;
+    } else {
+      E* dst = static_cast<E*>(a.means) + ((size_t(h) * a.M + m) * 2 + which) * kHeadDim + ch;
+      store_elem(dst, s / float(frame_dropped(a.g, f)));
+    }
   }
+}
+
+struct ReduceArgs {
+  const float* partial;  // [H][F][2][64]
+  void* means;           // [H][1][2][64] input type
+  int F;
+  float count;           // tokens the mean stands for (exact: < 2^24)
+};
+
+template <typename E>
+__global__ __launch_bounds__(128) void means_reduce_kernel(ReduceArgs a) {
+  const int h = blockIdx.x, tid = threadIdx.x;  // tid = which * 64 + channel
+  const float* src = a.partial + size_t(h) * a.F * 2 * kHeadDim + tid;
+  float s = 0.f;
+  for (int m = 0; m < a.F; ++m) s += src[size_t(m) * 2 * kHeadDim];
+  store_elem(static_cast<E*>(a.means) + size_t(h) * 2 * kHeadDim + tid, s / a.count);
 }
 
 struct PackArgs {
@@ -106,7 +138,6 @@ struct PackArgs {
   int g2f;
   int segment_rows;
   int frames;
-  int dropped;
   IndexGeom g;
 };
 
@@ -168,7 +199,7 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a) {
   }
   if (a.dcount && h == 0 && tile == 0) {
     for (int f = tid; f < a.frames; f += 256)
-      a.dcount[f] = (a.g.subsampled && !(a.g.ref_dense && f == 0)) ? a.dropped : 0;
+      a.dcount[f] = frame_dropped(a.g, f);
   }
   if constexpr (TRANSPOSE_V) {
     __syncthreads();
@@ -193,19 +224,34 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a) {
 hipError_t launch_means(const vggt_attn_plan_s& p, const void* k, const void* v, void* ws,
                         hipStream_t stream) {
   if (p.M == 0) return hipSuccess;
+  const bool single = p.mean_global || p.g2m;
+  char* base = static_cast<char*>(ws);
   MeansArgs a{};
   a.k = k;
   a.v = v;
-  a.means = static_cast<char*>(ws) + p.layout.off_means;
+  a.means = base + p.layout.off_means;
+  a.partial = single ? reinterpret_cast<float*>(base + p.layout.off_partial) : nullptr;
   a.T = p.T;
   a.M = int(p.M);
-  a.dropped = int(p.dropped);
+  a.F = int(p.M_frames);
   a.g = p.geom;
-  const dim3 grid(unsigned(p.M), unsigned(p.heads));
-  if (p.in_dtype == VGGT_ATTN_BF16)
+  const dim3 grid(unsigned(p.M_frames), unsigned(p.heads));
+  const bool bf16 = p.in_dtype == VGGT_ATTN_BF16;
+  if (bf16)
     hipLaunchKernelGGL(means_kernel<uint16_t>, grid, dim3(256), 0, stream, a);
   else
     hipLaunchKernelGGL(means_kernel<float>, grid, dim3(256), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !single) return e;
+  ReduceArgs r{};
+  r.partial = a.partial;
+  r.means = a.means;
+  r.F = a.F;
+  r.count = float(p.dropped_total);
+  if (bf16)
+    hipLaunchKernelGGL(means_reduce_kernel<uint16_t>, dim3(unsigned(p.heads)), dim3(128), 0, stream, r);
+  else
+    hipLaunchKernelGGL(means_reduce_kernel<float>, dim3(unsigned(p.heads)), dim3(128), 0, stream, r);
   return hipGetLastError();
 }
 
@@ -227,7 +273,6 @@ hipError_t launch_pack(const vggt_attn_plan_s& p, const void* k, const void* v, 
   a.g2f = p.g2f ? 1 : 0;
   a.segment_rows = int(p.segment_rows);
   a.frames = p.frames;
-  a.dropped = int(p.dropped);
   a.g = p.geom;
   const dim3 grid(unsigned(p.rows_per_head / kTile), unsigned(p.heads));
   if (p.in_dtype == VGGT_ATTN_BF16)

@@ -17,17 +17,27 @@ constexpr int64_t kMaxTokens = 8000000;
 constexpr int kMaxHeads = 4096;
 constexpr int64_t kMaxPackedRows = 16000000;  // per head, keeps row*64 within int32
 
-// Geometry the device code needs to enumerate S and to test membership in closed form.
+constexpr int kMaxPhases = 9;  // s_h * s_w for the largest window (3 x 3)
+
+// Geometry the device code needs to enumerate S and the mean frames and to test membership in
+// closed form.  Compressed frame f has grid phase k = f mod nphase (nphase = s_h*s_w with the
+// phase-shifted grid, else 1), row offset k / s_w and column offset k % s_w; every quantity of
+// a compressed frame depends on f only through k.
 struct IndexGeom {
   int L;           // tokens per frame
   int P;           // patches per frame
   int n_special;   // camera/register tokens per frame (slots 0 .. n_special-1)
   int grid_w;      // patch columns
   int s_h, s_w;    // window (row stride, column stride)
-  int kw;          // kept columns per compressed frame = ceil(grid_w / s_w)
-  int kept;        // kept patches per compressed frame = ceil(grid_h/s_h)*ceil(grid_w/s_w)
   int ref_dense;   // frame 0 dense
   int subsampled;  // sigma > 1
+  int g2m;         // every token feeds one mean, none is kept
+  int f0;          // first compressed frame (1 with a dense frame 0, else 0)
+  int nphase;      // grid phases (1 without the phase shift)
+  int rows_of[3];  // kept rows for row offset ro: ceil((grid_h - ro) / s_h)
+  int cols_of[3];  // kept columns for column offset co: ceil((grid_w - co) / s_w)
+  int cprefix[kMaxPhases + 1];  // S entries of compressed frames of phases 0..k-1 (one each)
+  int mprefix[kMaxPhases + 1];  // phases 0..k-1 whose frames have a nonempty dropped set
 };
 
 }  // namespace vggt
@@ -39,11 +49,16 @@ struct vggt_attn_plan_s {
   int in_dtype, out_dtype;
   // derived
   bool g2f, ref_dense, diag, mean, mean_count, subsampled, prescale_q;
-  int s_h, s_w, L, P, kh, kw, kept;
+  bool phase, mean_global, g2m;
+  int s_h, s_w, L, P;
   int64_t T;
-  int64_t dropped;        // |D_f| of a compressed frame
+  int64_t dropped_of_phase[vggt::kMaxPhases];  // |D_f| of a compressed frame of phase k
   int64_t n_dense_frames, n_compressed_frames;
+  int64_t dropped_total;  // sum of |D_f| over all frames (G2M: T)
   int64_t nS, M, n_diag;
+  int64_t M_frames;       // frames feeding a mean (nonempty dropped set; G2M: every frame)
+  double mean_bias_s[vggt::kMaxPhases];  // per phase (per-frame scope) or [0] (single mean):
+                                         // COUNT bias in raw-score units, ln(n) / tau
   int64_t segments, segment_rows, keys_per_segment, n_plain, rows_per_head;
   double flops;
   size_t elem_bytes;
