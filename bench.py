@@ -45,16 +45,42 @@ WORKLOADS = {
                  "200 frames x 1374 tokens, 16 heads, d=64, bf16 in / fp32 out, Global-to-Frame (3200 batches of 1374x1374)"),
     "sga9-200f": (dict(frames=200, grid_h=37, grid_w=37, heads=16, sigma=9, diag=True, mean=True),
                   "200 frames x 1374 tokens, 16 heads, d=64, bf16 in / fp32 out, SGA sigma=9 (3x3), diag + mean"),
+    "sga6-800f-phase": (dict(frames=800, grid_h=37, grid_w=37, heads=16, sigma=6, diag=True, mean=True, phase_shift=True),
+                        "800 frames x 1374 tokens, 16 heads, d=64, bf16 in / fp32 out, SGA sigma=6 (2x3) on a "
+                        "phase-shifted grid (offsets cycle over 6 frames), frame 0 + specials dense, diag + per-frame mean"),
+    "sga9-200f-phase-global": (dict(frames=200, grid_h=37, grid_w=37, heads=16, sigma=9, diag=True, mean=True,
+                                    mean_count=True, mean_global=True, phase_shift=True),
+                               "200 frames x 1374 tokens, 16 heads, d=64, bf16 in / fp32 out, SGA sigma=9 (3x3) on a "
+                               "phase-shifted grid, diag + one global mean K/V with the log-count bias"),
+    "g2m-32f": (dict(frames=32, grid_h=37, grid_w=37, heads=16, g2m=True),
+                "32 frames x 1374 tokens, 16 heads, d=64, bf16 in / fp32 out, Global-to-Mean (one mean K/V token)"),
 }
 
-# Reported beside the headline workload (same run, fewer steps).  The 200-frame pair runs G2F and
-# then SGA sigma 9 on the same tensors, the early/middle layer split.
+# Reported beside the headline workload (same run, fewer steps).  Each group shares one set of
+# tensors: the 200-frame group runs G2F and then SGA sigma 9 (plain, then on the phase-shifted
+# grid with one global mean), the early/middle layer split.
 EXTRA_GROUPS = [
     ("tiny-fp32", [dict(frames=4, grid_h=8, grid_w=8, heads=2, sigma=4, diag=True, mean=True)], "fp32"),
-    ("dense-32f", [WORKLOADS["dense-32f"][0]], "bf16"),
+    ("dense+g2m-32f", [WORKLOADS["dense-32f"][0], WORKLOADS["g2m-32f"][0]], "bf16"),
     ("sga4-100f", [WORKLOADS["sga4-100f"][0]], "bf16"),
-    ("g2f+sga9-200f", [WORKLOADS["g2f-200f"][0], WORKLOADS["sga9-200f"][0]], "bf16"),
+    ("g2f+sga9-200f", [WORKLOADS["g2f-200f"][0], WORKLOADS["sga9-200f"][0], WORKLOADS["sga9-200f-phase-global"][0]],
+     "bf16"),
 ]
+# Run on the headline workload's own tensors (same geometry), before they are released.
+SAME_TENSOR_EXTRAS = {"sga6-800f": ["sga6-800f-phase"], "sga6-800f-phase": ["sga6-800f"]}
+
+
+def form_name(d) -> str:
+    if d.get("g2f"):
+        return "g2f"
+    if d.get("g2m"):
+        return "g2m"
+    name = f"sigma{d.get('sigma', 1)}"
+    if d.get("phase_shift"):
+        name += "-phase"
+    if d.get("mean_global"):
+        name += "-globalmean"
+    return name
 
 KERNEL_SOURCES = ("vggt_global_attention_attn_amd/csrc/attn.hip", "vggt_global_attention_attn_amd/csrc/device_common.h")
 TRAFFIC_FILE = "profiles/attn_{workload}_hbm_traffic.txt"
@@ -130,11 +156,33 @@ def time_calls(plans, tensors, outs, wss, steps, warmup):
     return wall, attn
 
 
+def timed_group(dev, name, descs, dtype, tensors, steps):
+    """Time the forwards of one group of plans on shared tensors; one result entry."""
+    import torch
+
+    import vggt_global_attention_attn_amd as va
+
+    plans = [va.Plan(**d, in_dtype=dtype, out_dtype="fp32") for d in descs]
+    outs = [p.new_output(dev) for p in plans]
+    wss = [p.new_workspace(dev) for p in plans]
+    wall, attn = time_calls(plans, tensors, outs, wss, steps, warmup=1)
+    flops = [p.counts()["flops"] for p in plans]
+    T = plans[0].T
+    entry = {"name": name, "ms_per_step": wall * 1e3, "queries_per_s": T / wall,
+             "tflops": sum(flops) / wall / 1e12, "pct_bf16_peak": 100 * sum(flops) / wall / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+             "attention": [{"form": form_name(d), "ms": a * 1e3, "kv_tokens": p.counts()["n_kv"],
+                            "tflops": f / a / 1e12, "frac_bf16_peak": f / a / 1e12 / MFMA_BF16_PEAK_TFLOPS}
+                           for d, a, f, p in zip(descs, attn, flops, plans)]}
+    log(f"extra {name}: {wall * 1e3:.3f} ms/step, {entry['tflops']:.1f} TFLOP/s")
+    del outs, wss
+    torch.cuda.empty_cache()
+    return entry
+
+
 def extra_workloads(dev, steps: int):
     import numpy as np
     import torch
 
-    import vggt_global_attention_attn_amd as va
     from synth import make_qkv
 
     results = []
@@ -146,20 +194,8 @@ def extra_workloads(dev, steps: int):
         else:
             up = lambda x: torch.from_numpy(x).to(dev)
         tensors = (up(q), up(k), up(v))
-        plans = [va.Plan(**d, in_dtype=dtype, out_dtype="fp32") for d in descs]
-        outs = [p.new_output(dev) for p in plans]
-        wss = [p.new_workspace(dev) for p in plans]
-        wall, attn = time_calls(plans, tensors, outs, wss, steps, warmup=1)
-        flops = [p.counts()["flops"] for p in plans]
-        T = plans[0].T
-        entry = {"name": name, "ms_per_step": wall * 1e3, "queries_per_s": T / wall,
-                 "tflops": sum(flops) / wall / 1e12, "pct_bf16_peak": 100 * sum(flops) / wall / 1e12 / MFMA_BF16_PEAK_TFLOPS,
-                 "attention": [{"form": ("g2f" if d.get("g2f") else f"sigma{d.get('sigma', 1)}"), "ms": a * 1e3,
-                                "tflops": f / a / 1e12, "frac_bf16_peak": f / a / 1e12 / MFMA_BF16_PEAK_TFLOPS}
-                               for d, a, f in zip(descs, attn, flops)]}
-        results.append(entry)
-        log(f"extra {name}: {wall * 1e3:.3f} ms/step, {entry['tflops']:.1f} TFLOP/s")
-        del tensors, outs, wss
+        results.append(timed_group(dev, name, descs, dtype, tensors, steps))
+        del tensors
         torch.cuda.empty_cache()
     return results
 
@@ -171,7 +207,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="sga6-800f", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=256, help="query rows in the oracle sample")
+    ap.add_argument("--cpu-rows", type=int, default=1024, help="query rows in the oracle sample")
     ap.add_argument("--no-extra", action="store_true", help="skip the other workloads")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (PMC scale calibration)")
@@ -266,8 +302,8 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": description, "name": args.workload, "frames": desc["frames"], "tokens": T,
-                   "heads": H, "head_dim": 64, "sigma": desc.get("sigma", 1), "kv_tokens": counts["n_kv"],
+        "config": {"workload": description, "name": args.workload, "form": form_name(desc), "frames": desc["frames"],
+                   "tokens": T, "heads": H, "head_dim": 64, "sigma": desc.get("sigma", 1), "kv_tokens": counts["n_kv"],
                    "mean_tokens": counts["n_mean"], "diag_queries": counts["n_diag"]},
         "query_heads_per_s": H * T / step_s,
         "tflops": flops / step_s / 1e12,
@@ -282,9 +318,13 @@ def main() -> int:
     }
 
     if not args.no_extra:
-        del out, ws, qd, kd, vd
+        del out, ws
         torch.cuda.empty_cache()
-        result["other_workloads"] = extra_workloads(dev, steps=3)
+        same = [timed_group(dev, n, [WORKLOADS[n][0]], "bf16", (qd, kd, vd), steps=3)
+                for n in SAME_TENSOR_EXTRAS.get(args.workload, [])]
+        del qd, kd, vd
+        torch.cuda.empty_cache()
+        result["other_workloads"] = same + extra_workloads(dev, steps=3)
 
     if not args.no_cpu_baseline:
         import oracle

@@ -4,17 +4,18 @@
 // Operation: "AVGGT: Rethinking Global Attention for Accelerating VGGT" (papernotes.org CVPR
 // 2026 notes), 关键设计 2 (the attention equation over the kept set S), 关键设计 3 (diagonal
 // self term and mean K/V share one softmax normalisation), 关键设计 1 (Global-to-Frame: keys of
-// a query are the tokens of its own frame); "RegimeVGGT ..." (papernotes.org NeurIPS 2026
-// notes), 关键设计 2 (a key standing for g tokens carries +ln g on its logit -- used for the
-// COUNT weighting of the mean keys).
+// a query are the tokens of its own frame), ablation table (G2M: a single mean key); "RegimeVGGT
+// ..." (papernotes.org NeurIPS 2026 notes), 关键设计 2 (a key standing for g tokens carries +ln g
+// on its logit -- used for the COUNT weighting of the mean keys), 关键设计 3 (per-frame phase of
+// the sampling grid, which sets |D_f| and so the bias of each frame's mean key).
 //
 // attn_bf16_kernel: flash-style forward on the bf16 matrix cores (v_mfma_f32_16x16x32_bf16,
 // float32 accumulation).  A work-group of 4 waves owns BM = 4*16*QB query rows of one head and
-// streams the key segment in 64-key tiles through LDS filled by direct global->LDS copies.  Scores are formed
-// transposed, S^T = K Q^T, so each lane holds 4 keys x 1 query per 16x16 block: the row max
-// is a 16-value in-lane max plus two cross-lane steps, the row sum stays lane-local until the
-// epilogue, and the bf16 probabilities are already laid out as the B operand of
-// O^T = V^T P^T (the packed value tiles store keys in the matching order).
+// streams the key segment in 64-key tiles through LDS filled by direct global->LDS copies.
+// Scores are formed transposed, S^T = K Q^T, so each lane holds 4 keys x 1 query per 16x16
+// block: the row max is a 16-value in-lane max plus two cross-lane steps, the row sum stays
+// lane-local until the epilogue, and the bf16 probabilities are already laid out as the B
+// operand of O^T = V^T P^T (the packed value tiles store keys in the matching order).
 //
 // attn_f32_kernel: float32 path (fp32 inputs and outputs), one lane per query, keys through LDS.
 #include <hip/hip_runtime.h>
