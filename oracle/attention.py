@@ -50,6 +50,10 @@ notes of the repository):
       over all T tokens (specials included); the output of every query is that mean value.
   R22 a frame whose dropped set is empty (possible under the phase shift on one-patch-wide
       grids) contributes no mean term.
+  R23 size-aware keys ([Regime] 关键设计 2): the caller gives log g_t per token (natural log,
+      finite, shared by all heads); the logit of every token key -- S, the diagonal self term,
+      G2F's frame keys -- gets + log g_t.  Not combined with a mean term or G2M (the pages do not
+      say how sizes enter a mean).
 
 Parity: these functions are pinned by tests against torch's scaled-dot-product attention on
 explicitly built key lists, closed-form counts, hand-enumerated index sets and exact identities.
@@ -87,6 +91,7 @@ class Desc:
     phase_shift: bool = False  # per-frame offset of the sampling grid (reading R19)
     mean_global: bool = False  # one mean over all dropped patches instead of one per frame (R20)
     g2m: bool = False          # K/V = one mean token over all tokens (R21)
+    log_size: bool = False     # token keys carry a caller-supplied log-size bias (R23)
 
     def __post_init__(self):
         if self.sigma not in SIGMA_WINDOWS:
@@ -97,6 +102,8 @@ class Desc:
             raise ValueError("G2M takes no subsampling, diagonal, per-frame mean or G2F")
         if self.mean_global and not self.mean:
             raise ValueError("mean_global selects the scope of the mean term; it needs mean=True")
+        if self.log_size and (self.mean or self.g2m):
+            raise ValueError("log-size keys are not combined with a mean term or G2M")
         if min(self.frames, self.grid_h, self.grid_w, self.heads, self.head_dim) < 1 or self.n_special < 0:
             raise ValueError("sizes must be positive")
 
@@ -239,7 +246,18 @@ def frame_means(k: np.ndarray, v: np.ndarray, desc: Desc):
 # Attention, gather formulation
 # ----------------------------------------------------------------------------------------------
 
-def attention(q, k, v, desc: Desc, rows=None, workers: int = 1, chunk: int = 256) -> np.ndarray:
+def _log_sizes(desc: Desc, log_g):
+    """float64 [T] per-token log sizes: the given ones (R23), zeros without the size option."""
+    if not desc.log_size:
+        if log_g is not None:
+            raise ValueError("log_g given for a descriptor without log_size")
+        return np.zeros(desc.T)
+    if log_g is None or np.shape(log_g) != (desc.T,):
+        raise ValueError("log_size needs log_g of shape [T]")
+    return np.asarray(log_g, dtype=np.float64)
+
+
+def attention(q, k, v, desc: Desc, rows=None, workers: int = 1, chunk: int = 256, log_g=None) -> np.ndarray:
     """out[h, i, :] for query token rows[i] (all tokens if rows is None), float64 [H][R][d].
 
     GLOBAL form ([AVGGT-zh] 关键设计 2, the attention equation; reading R7): for query q of
@@ -251,13 +269,15 @@ def attention(q, k, v, desc: Desc, rows=None, workers: int = 1, chunk: int = 256
     and the output is the softmax-weighted sum of the values under one joint normalisation.
     G2F form ([AVGGT-zh] 关键设计 1): the keys of a query are the L tokens of its own frame.
     G2M form (R21): a softmax over one key, so every output row is the mean value.
-    sigma = 1 gives S = every token: plain global attention."""
+    sigma = 1 gives S = every token: plain global attention.
+    With log_size, the logit of token key t also gets + log_g[t] ([Regime] 关键设计 2, R23)."""
     H, T, d = q.shape
     if T != desc.T or H != desc.heads or d != desc.head_dim:
         raise ValueError("q shape does not match the descriptor")
     rows = np.arange(T, dtype=np.int64) if rows is None else np.asarray(rows, dtype=np.int64)
     out = np.empty((H, rows.size, d))
     tau = desc.tau
+    lg_size = _log_sizes(desc, log_g)
 
     if desc.g2m:
         vbar = frame_means(k, v, desc)[1]
@@ -272,9 +292,10 @@ def attention(q, k, v, desc: Desc, rows=None, workers: int = 1, chunk: int = 256
                 sel = np.flatnonzero(frame_of == f)
                 kf = as_f64(k[h, f * desc.L:(f + 1) * desc.L])
                 vf = as_f64(v[h, f * desc.L:(f + 1) * desc.L])
+                bias = lg_size[f * desc.L:(f + 1) * desc.L]
                 for c0 in range(0, sel.size, chunk):
                     s = sel[c0:c0 + chunk]
-                    lg = tau * (as_f64(q[h, rows[s]]) @ kf.T)
+                    lg = tau * (as_f64(q[h, rows[s]]) @ kf.T) + bias[None, :]
                     out[h, s] = _joint_softmax([(lg, vf)])
     else:
         S = index_set(desc)
@@ -287,12 +308,12 @@ def attention(q, k, v, desc: Desc, rows=None, workers: int = 1, chunk: int = 256
             for c0 in range(0, rows.size, chunk):
                 r = rows[c0:c0 + chunk]
                 qr = as_f64(q[h, r])
-                parts = [(tau * (qr @ kS.T), vS)]
+                parts = [(tau * (qr @ kS.T) + lg_size[S][None, :], vS)]
                 if kbar.shape[1]:
                     parts.append((tau * (qr @ kbar[h].T) + beta[None, :], vbar[h]))
                 if desc.diag:
                     own_k, own_v = as_f64(k[h, r]), as_f64(v[h, r])
-                    ls = np.where(keep[r], -np.inf, tau * np.einsum("rd,rd->r", qr, own_k))
+                    ls = np.where(keep[r], -np.inf, tau * np.einsum("rd,rd->r", qr, own_k) + lg_size[r])
                     parts.append((ls[:, None], own_v[:, None, :]))
                 out[h, c0:c0 + r.size] = _joint_softmax(parts)
 
@@ -343,7 +364,7 @@ def kept_mask_by_sets(desc: Desc) -> np.ndarray:
     return keep
 
 
-def attention_bruteforce(q, k, v, desc: Desc) -> np.ndarray:
+def attention_bruteforce(q, k, v, desc: Desc, log_g=None) -> np.ndarray:
     """Same operation as attention(), written as one masked softmax over T + N columns.
 
     Columns 0..T-1 are the tokens; column T+f is frame f's mean K/V, built with an averaging
@@ -351,10 +372,12 @@ def attention_bruteforce(q, k, v, desc: Desc) -> np.ndarray:
     is in S, or (DIAG) it is the row's own token and that token is not in S; under G2F a token
     column is open iff it lies in the row's frame.  A mean column is open when MEAN is on and
     |D_f| > 0, with bias ln|D_f| under COUNT.  Global mean scope and G2M use one mean column
-    whose row of A averages every token outside S.  Meant for T up to a few thousand."""
+    whose row of A averages every token outside S.  Token column t carries + log_g[t] under the
+    size option.  Meant for T up to a few thousand."""
     H, T, d = q.shape
     q64, k64, v64 = as_f64(q), as_f64(k), as_f64(v)
     N, L = desc.frames, desc.L
+    lg_size = _log_sizes(desc, log_g)
     frame = np.arange(T) // L
     if desc.g2f:
         open_tok = frame[:, None] == frame[None, :]
@@ -385,6 +408,7 @@ def attention_bruteforce(q, k, v, desc: Desc) -> np.ndarray:
         vals = np.concatenate([v64[h], A @ v64[h]], axis=0)
         lg = desc.tau * (q64[h] @ keys.T)
         lg[:, T:] += bias[None, :]
+        lg[:, :T] += lg_size[None, :]
         lg = np.where(mask, lg, -np.inf)
         w = np.exp(lg - lg.max(axis=1, keepdims=True))
         w /= w.sum(axis=1, keepdims=True)

@@ -36,6 +36,7 @@ __all__ = [
     "make_qkv",
     "sample_rows",
     "host_threads",
+    "make_log_sizes",
 ]
 
 
@@ -128,3 +129,12 @@ def sample_rows(frames: int, grid_h: int, grid_w: int, n_special: int, count: in
     pool = np.setdiff1d(np.arange(T, dtype=np.int64), forced, assume_unique=True)
     draw = np.random.Generator(np.random.PCG64(seed)).choice(pool, size=min(rest, pool.size), replace=False)
     return np.unique(np.concatenate([forced, draw.astype(np.int64)]))
+
+
+def make_log_sizes(frames: int, grid_h: int, grid_w: int, n_special: int, seed: int = 0, max_size: int = 4):
+    """Per-token group sizes g (int64, uniform in 1..max_size) and their natural logs as float32,
+    the form in which a caller hands sizes to the library: synthetic stand-ins for the token
+    counts behind merged tokens.  One PCG64 stream, spawn_key=(3, 0)."""
+    T = frames * tokens_per_frame(grid_h, grid_w, n_special)
+    g = _rng(seed, 3, 0).integers(1, max_size + 1, size=T, dtype=np.int64)
+    return g, np.log(g.astype(np.float64)).astype(np.float32)

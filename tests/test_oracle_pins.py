@@ -13,7 +13,9 @@ Each check ties the oracle to a fact the pages fix or to an independent route:
     page's offset formula for square windows, and the coverage the page states (consecutive
     frames' grids together cover every patch);
   * for the global mean scope and G2M: explicit key lists through torch SDPA, and the collapse
-    identity (identical keys give uniform weights, so attention returns the mean value).
+    identity (identical keys give uniform weights, so attention returns the mean value);
+  * for size-aware keys (RegimeVGGT notes, 关键设计 2): a key standing for g tokens equals g
+    copies of it in a plain attention (integer g, through torch SDPA).
 """
 import math
 import os
@@ -24,7 +26,7 @@ import torch
 
 import oracle
 from oracle import Desc
-from synth import bf16_bits_to_f32, f32_to_bf16_bits, make_qkv, sample_rows
+from synth import bf16_bits_to_f32, f32_to_bf16_bits, make_log_sizes, make_qkv, sample_rows
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -509,3 +511,84 @@ def test_sample_rows_forced_and_seeded():
         for j in range(5):
             assert f * L + j in set(r1.tolist())
         assert f * L + 5 + 36 * 37 + 36 in set(r1.tolist())  # last patch of the frame
+
+
+# ------------------------------------------------------------------------------------------
+# Size-aware keys: + log g on the logit (RegimeVGGT notes, 关键设计 2)
+# ------------------------------------------------------------------------------------------
+
+def _sizes(d, seed=0):
+    g, _ = make_log_sizes(d.frames, d.grid_h, d.grid_w, d.n_special, seed=seed)
+    return g, np.log(g.astype(np.float64))
+
+
+def test_log_size_dense_is_replicated_keys():
+    """Dense attention where key t carries + ln g_t equals plain attention over a key list in
+    which token t appears g_t times."""
+    d = Desc(frames=3, grid_h=4, grid_w=5, heads=2, sigma=1, log_size=True)
+    q, k, v = inputs(d, seed=31)
+    g, lg = _sizes(d, seed=1)
+    assert set(np.unique(g).tolist()) == {1, 2, 3, 4}
+    rep = np.repeat(np.arange(d.T), g)
+    ref = sdpa(f64(q), f64(k)[:, rep], f64(v)[:, rep])
+    np.testing.assert_allclose(oracle.attention(q, k, v, d, log_g=lg), ref, rtol=0, atol=1e-12)
+
+
+def test_log_size_sga_with_diag_is_replicated_keys():
+    """SGA with the diagonal term: every key of S and the self term of a dropped query stand for
+    their g copies."""
+    d = Desc(**GOLD_DESC, diag=True, log_size=True)
+    q, k, v = inputs(d, seed=32)
+    g, lg = _sizes(d, seed=2)
+    S = hand_S()
+    Sset = set(S.tolist())
+    qf, kf, vf = f64(q), f64(k), f64(v)
+    out = oracle.attention(q, k, v, d, log_g=lg)
+    for r in range(0, d.T, 2):
+        keys = S if r in Sset else np.append(S, r)
+        rep = np.repeat(keys, g[keys])
+        ref = sdpa(qf[:, r:r + 1], kf[:, rep], vf[:, rep])[:, 0]
+        np.testing.assert_allclose(out[:, r], ref, rtol=0, atol=1e-12)
+
+
+def test_log_size_g2f_is_replicated_keys_per_frame():
+    d = Desc(frames=3, grid_h=3, grid_w=5, heads=2, g2f=True, log_size=True)
+    q, k, v = inputs(d, seed=33)
+    g, lg = _sizes(d, seed=3)
+    out = oracle.attention(q, k, v, d, log_g=lg)
+    for f in range(d.frames):
+        tok = np.arange(f * d.L, (f + 1) * d.L)
+        rep = np.repeat(tok, g[tok])
+        ref = sdpa(f64(q)[:, tok], f64(k)[:, rep], f64(v)[:, rep])
+        np.testing.assert_allclose(out[:, tok], ref, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("flags", [dict(sigma=1), dict(g2f=True), dict(sigma=6, diag=True),
+                                   dict(sigma=9, diag=True, ref_dense=False, phase_shift=True)])
+@pytest.mark.parametrize("geom", [(3, 5, 7), (2, 7, 4)])
+def test_log_size_bruteforce_matches_gather(flags, geom):
+    N, gh, gw = geom
+    d = Desc(frames=N, grid_h=gh, grid_w=gw, heads=2, log_size=True, **flags)
+    q, k, v = inputs(d, seed=34)
+    _, lg = _sizes(d, seed=4)
+    np.testing.assert_allclose(oracle.attention(q, k, v, d, log_g=lg),
+                               oracle.attention_bruteforce(q, k, v, d, log_g=lg), rtol=0, atol=1e-12)
+
+
+def test_log_size_unit_sizes_change_nothing():
+    d = Desc(frames=3, grid_h=5, grid_w=7, heads=2, sigma=4, diag=True, log_size=True)
+    q, k, v = inputs(d, seed=35)
+    plain = Desc(frames=3, grid_h=5, grid_w=7, heads=2, sigma=4, diag=True)
+    np.testing.assert_allclose(oracle.attention(q, k, v, d, log_g=np.zeros(d.T)), oracle.attention(q, k, v, plain),
+                               rtol=0, atol=1e-14)
+
+
+def test_log_size_descriptor_rules():
+    with pytest.raises(ValueError):
+        Desc(frames=2, grid_h=4, grid_w=4, heads=1, sigma=4, mean=True, log_size=True)
+    with pytest.raises(ValueError):
+        Desc(frames=2, grid_h=4, grid_w=4, heads=1, g2m=True, log_size=True)
+    d = Desc(frames=2, grid_h=4, grid_w=4, heads=1, sigma=4, log_size=True)
+    q, k, v = inputs(d)
+    with pytest.raises(ValueError):
+        oracle.attention(q, k, v, d)  # sizes missing
