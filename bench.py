@@ -52,6 +52,9 @@ WORKLOADS = {
                                     mean_count=True, mean_global=True, phase_shift=True),
                                "200 frames x 1374 tokens, 16 heads, d=64, bf16 in / fp32 out, SGA sigma=9 (3x3) on a "
                                "phase-shifted grid, diag + one global mean K/V with the log-count bias"),
+    "sga6-800f-sized": (dict(frames=800, grid_h=37, grid_w=37, heads=16, sigma=6, diag=True, log_size=True),
+                        "800 frames x 1374 tokens, 16 heads, d=64, bf16 in / fp32 out, SGA sigma=6 (2x3) with the "
+                        "diagonal term and size-aware keys (seeded group sizes 1..4, + ln g on every key's logit)"),
     "g2m-32f": (dict(frames=32, grid_h=37, grid_w=37, heads=16, g2m=True),
                 "32 frames x 1374 tokens, 16 heads, d=64, bf16 in / fp32 out, Global-to-Mean (one mean K/V token)"),
 }
@@ -67,7 +70,7 @@ EXTRA_GROUPS = [
      "bf16"),
 ]
 # Run on the headline workload's own tensors (same geometry), before they are released.
-SAME_TENSOR_EXTRAS = {"sga6-800f": ["sga6-800f-phase"], "sga6-800f-phase": ["sga6-800f"]}
+SAME_TENSOR_EXTRAS = {"sga6-800f": ["sga6-800f-phase", "sga6-800f-sized"], "sga6-800f-phase": ["sga6-800f"]}
 
 
 def form_name(d) -> str:
@@ -80,7 +83,25 @@ def form_name(d) -> str:
         name += "-phase"
     if d.get("mean_global"):
         name += "-globalmean"
+    if d.get("log_size"):
+        name += "-sized"
     return name
+
+
+class Sized:
+    """Wraps a LOG_SIZE plan so that time_calls can call pack/forward without log sizes."""
+
+    def __init__(self, plan, log_g):
+        self.plan, self.log_g = plan, log_g
+
+    def __getattr__(self, name):
+        return getattr(self.plan, name)
+
+    def forward(self, q, k, v, out, ws):
+        self.plan.forward_sized(q, k, v, self.log_g, out, ws)
+
+    def pack(self, k, v, ws):
+        self.plan.pack_sized(k, v, self.log_g, ws)
 
 KERNEL_SOURCES = ("vggt_global_attention_attn_amd/csrc/attn.hip", "vggt_global_attention_attn_amd/csrc/device_common.h")
 TRAFFIC_FILE = "profiles/attn_{workload}_hbm_traffic.txt"
@@ -163,6 +184,12 @@ def timed_group(dev, name, descs, dtype, tensors, steps):
     import vggt_global_attention_attn_amd as va
 
     plans = [va.Plan(**d, in_dtype=dtype, out_dtype="fp32") for d in descs]
+    if any(d.get("log_size") for d in descs):
+        from synth import make_log_sizes
+        d0 = descs[0]
+        _, lg = make_log_sizes(d0["frames"], d0["grid_h"], d0["grid_w"], 5, seed=5)
+        lg = torch.from_numpy(lg).to(dev)
+        plans = [Sized(p, lg) if d.get("log_size") else p for p, d in zip(plans, descs)]
     outs = [p.new_output(dev) for p in plans]
     wss = [p.new_workspace(dev) for p in plans]
     wall, attn = time_calls(plans, tensors, outs, wss, steps, warmup=1)
@@ -231,6 +258,11 @@ def main() -> int:
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     plan = va.Plan(**desc, in_dtype="bf16", out_dtype="fp32")
+    log_g = None
+    if desc.get("log_size"):
+        from synth import make_log_sizes
+        _, log_g = make_log_sizes(desc["frames"], desc["grid_h"], desc["grid_w"], 5, seed=5)
+        plan = Sized(plan, torch.from_numpy(log_g).to(dev))
     counts = plan.counts()
     T, H = plan.T, plan.heads
 
@@ -333,7 +365,7 @@ def main() -> int:
         cores = host_threads()
         log(f"oracle on {rows.size} rows x {H} heads with {cores} threads")
         c0 = time.perf_counter()
-        ref = oracle.attention(q, k, v, odesc, rows=rows, workers=cores)
+        ref = oracle.attention(q, k, v, odesc, rows=rows, workers=cores, log_g=log_g)
         c_s = time.perf_counter() - c0
         got = out_rows
         diff = got - ref

@@ -21,7 +21,9 @@
  *                is that mean value.
  * Two options refine SGA: a phase-shifted sampling grid (RegimeVGGT notes, 关键设计 3: the grid
  * of frame f is offset per frame so that consecutive frames together cover every patch) and a
- * global scope for the mean term (one mean over every dropped patch of every frame).
+ * global scope for the mean term (one mean over every dropped patch of every frame).  Size-aware
+ * keys (RegimeVGGT notes, 关键设计 2): with LOG_SIZE each token carries a caller-supplied
+ * log g (the number of source tokens it stands for) added to its logit wherever it is a key.
  *
  * Conventions shared by every entry point
  *   - Tensors q, k, v, out are dense row-major [H][T][d], T = N*L, batch 1.  Within a frame
@@ -83,8 +85,12 @@ enum {
   VGGT_ATTN_MEAN_GLOBAL = 1u << 7, /* with MEAN: one mean K/V over the union of all frames'
                                      dropped patches instead of one per frame; MEAN_COUNT then adds
                                      ln(sum_f |D_f|).  Requires MEAN.                              */
-  VGGT_ATTN_G2M = 1u << 8          /* Global-to-Mean (see above); needs sigma == 1 and none of
+  VGGT_ATTN_G2M = 1u << 8,         /* Global-to-Mean (see above); needs sigma == 1 and none of
                                      G2F, DIAG, MEAN, MEAN_GLOBAL, PHASE_SHIFT.                     */
+  VGGT_ATTN_LOG_SIZE = 1u << 9     /* size-aware keys: the logit of token key t (in S, the diagonal
+                                     self term, a G2F frame) gets + log_g[t], log_g passed to the
+                                     *_sized entry points.  Not with MEAN or G2M (EINVAL); the
+                                     bf16 path then ignores PRESCALE_Q.                            */
 };
 
 typedef struct vggt_attn_plan_s vggt_attn_plan_t;
@@ -102,6 +108,9 @@ typedef struct {
   int64_t off_means;         /* [H][M][2][d] input dtype: mean key, mean value               */
   int64_t off_partial;       /* float [H][F][2][d]: per-frame sums of a global mean (F frames
                                 contribute; MEAN_GLOBAL and G2M only, else empty)             */
+  int64_t off_kbias;         /* float [segments*segment_rows]: logit bias of each packed key
+                                in raw-score units, log_g[t] * sqrt(d) (LOG_SIZE only)        */
+  int64_t off_logsize;       /* float [T]: copy of log_g (LOG_SIZE only)                      */
   int64_t off_kpack;         /* [H][segments*segment_rows][d] input dtype                    */
   int64_t off_vpack;         /* bf16: [H][rows/64][d][64] key-minor tiles (see below);
                                 fp32: [H][rows][d]                                           */
@@ -117,7 +126,7 @@ typedef struct {
  *     then have no effect: no token is dropped);
  *   G2F requires sigma == 1 and none of DIAG, MEAN, MEAN_GLOBAL, PHASE_SHIFT, G2M (EINVAL);
  *   G2M requires sigma == 1 and none of G2F, DIAG, MEAN, MEAN_GLOBAL, PHASE_SHIFT (EINVAL);
- *   MEAN_GLOBAL requires MEAN (EINVAL);
+ *   MEAN_GLOBAL requires MEAN (EINVAL); LOG_SIZE excludes MEAN and G2M (EINVAL);
  *   a mean key exists for each frame whose dropped set is nonempty (one in all under
  *     MEAN_GLOBAL and G2M); with PHASE_SHIFT a one-patch-wide grid can leave some frames'
  *     dropped sets empty;
@@ -144,7 +153,8 @@ int vggt_attn_counts(const vggt_attn_plan_t* plan, int64_t* n_kv, int64_t* n_mea
 /* Workspace layout of the plan (see vggt_attn_layout_t). */
 int vggt_attn_layout(const vggt_attn_plan_t* plan, vggt_attn_layout_t* out);
 
-/* Full forward: vggt_attn_pack followed by vggt_attn_attend on `stream`.
+/* Full forward: vggt_attn_pack followed by vggt_attn_attend on `stream` (not for LOG_SIZE plans:
+ * see vggt_attn_forward_sized).
  * q, k, v: [H][T][d] of the input dtype; out: [H][T][d] of the output dtype; every pointer
  * 16-byte aligned; out must not overlap q, k, v or the workspace (EALIAS). */
 int vggt_attn_forward(const vggt_attn_plan_t* plan, const void* q, const void* k, const void* v,
@@ -164,6 +174,19 @@ int vggt_attn_pack(const vggt_attn_plan_t* plan, const void* k, const void* v, v
  * same k, v (k and v are read again for the diagonal term).  Writes every element of out. */
 int vggt_attn_attend(const vggt_attn_plan_t* plan, const void* q, const void* k, const void* v,
                      void* out, const void* workspace, size_t workspace_bytes, void* stream);
+
+/* The same calls for a LOG_SIZE plan (vggt_attn_forward and vggt_attn_pack return EINVAL for
+ * one, and these return EINVAL for a plan without LOG_SIZE).  log_g: device float [T], 4-byte
+ * aligned, the natural log of the number of source tokens token t stands for (0 for a plain
+ * token), shared by all heads; values must be finite.  The pack stage copies what the attention
+ * stage needs into the workspace, so vggt_attn_attend takes no log_g.  out must not overlap
+ * log_g, and the workspace must not overlap log_g (EALIAS). */
+int vggt_attn_forward_sized(const vggt_attn_plan_t* plan, const void* q, const void* k,
+                            const void* v, const float* log_g, void* out, void* workspace,
+                            size_t workspace_bytes, void* stream);
+int vggt_attn_pack_sized(const vggt_attn_plan_t* plan, const void* k, const void* v,
+                         const float* log_g, void* workspace, size_t workspace_bytes,
+                         void* stream);
 
 /* Copy S (|S| int32, ascending token ids) and |D_f| (N int32) from a packed workspace to host
  * memory; waits for `stream`.  Either host pointer may be NULL.  Under G2F there is no S and

@@ -42,5 +42,5 @@ def plan_kwargs(desc, in_dtype="bf16", out_dtype="fp32"):
     return dict(frames=desc.frames, grid_h=desc.grid_h, grid_w=desc.grid_w, heads=desc.heads,
                 head_dim=desc.head_dim, n_special=desc.n_special, sigma=desc.sigma, ref_dense=desc.ref_dense,
                 diag=desc.diag, mean=desc.mean, mean_count=desc.mean_count, g2f=desc.g2f,
-                phase_shift=desc.phase_shift, mean_global=desc.mean_global, g2m=desc.g2m,
+                phase_shift=desc.phase_shift, mean_global=desc.mean_global, g2m=desc.g2m, log_size=desc.log_size,
                 in_dtype=in_dtype, out_dtype=out_dtype)

@@ -61,6 +61,9 @@ CONFIGS = [
     Desc(100, 37, 37, 16, sigma=4, mean=True, mean_global=True, mean_count=True),
     Desc(5, 6, 1, 2, sigma=2, diag=True, mean=True, phase_shift=True, ref_dense=False),  # empty dropped sets
     Desc(32, 37, 37, 16, g2m=True),
+    Desc(32, 37, 37, 16, sigma=1, log_size=True),
+    Desc(200, 37, 37, 16, g2f=True, log_size=True),
+    Desc(100, 37, 37, 16, sigma=4, diag=True, log_size=True, phase_shift=True),
 ]
 
 
@@ -69,7 +72,7 @@ CONFIGS = [
 def test_plan_counts_match_oracle(va, desc):
     p = va.Plan(desc.frames, desc.grid_h, desc.grid_w, desc.heads, sigma=desc.sigma, ref_dense=desc.ref_dense,
                 diag=desc.diag, mean=desc.mean, mean_count=desc.mean_count, g2f=desc.g2f,
-                phase_shift=desc.phase_shift, mean_global=desc.mean_global, g2m=desc.g2m)
+                phase_shift=desc.phase_shift, mean_global=desc.mean_global, g2m=desc.g2m, log_size=desc.log_size)
     c = p.counts()
     o = oracle.counts(desc)
     assert (c["n_kv"], c["n_mean"], c["n_diag"]) == (o["n_kv"], o["n_mean"], o["n_diag"])
@@ -81,8 +84,12 @@ def test_plan_counts_match_oracle(va, desc):
     assert c["flops"] == pytest.approx(flops, rel=1e-12)
     lay = p.layout()
     assert lay["segment_rows"] % 64 == 0 and lay["segment_rows"] >= lay["keys_per_segment"]
-    for key in ("off_index", "off_dcount", "off_means", "off_partial", "off_kpack", "off_vpack", "total_bytes"):
+    for key in ("off_index", "off_dcount", "off_means", "off_partial", "off_kbias", "off_logsize", "off_kpack",
+                "off_vpack", "total_bytes"):
         assert lay[key] % 256 == 0
+    if desc.log_size:
+        assert lay["off_logsize"] - lay["off_kbias"] >= 4 * lay["segments"] * lay["segment_rows"]
+        assert lay["off_kpack"] - lay["off_logsize"] >= 4 * desc.T
     assert lay["total_bytes"] == p.workspace_bytes
 
 
@@ -102,13 +109,15 @@ def test_config5_sizes(va):
     (dict(g2f=True, sigma=4), "EINVAL"),
     (dict(g2f=True, mean=True), "EINVAL"),
     (dict(in_dtype="fp32", out_dtype="bf16"), "EINVAL"),
-    (dict(flags=1 << 9), "EINVAL"),
+    (dict(flags=1 << 10), "EINVAL"),
     (dict(flags=1 << 12), "EINVAL"),
     (dict(g2m=True, sigma=4), "EINVAL"),
     (dict(g2m=True, diag=True), "EINVAL"),
     (dict(g2m=True, g2f=True), "EINVAL"),
     (dict(g2f=True, phase_shift=True), "EINVAL"),
     (dict(sigma=4, mean_global=True), "EINVAL"),  # MEAN_GLOBAL without MEAN
+    (dict(sigma=4, mean=True, log_size=True), "EINVAL"),
+    (dict(g2m=True, log_size=True), "EINVAL"),
     (dict(frames=0), "EINVAL"),
     (dict(heads=0), "EINVAL"),
     (dict(frames=6000, grid_h=37, grid_w=37), "EINVAL"),  # 8.2M tokens > limit
@@ -133,3 +142,18 @@ def test_null_arguments(va):
     assert L.vggt_attn_pack(p.handle, None, None, None, 0, None) == -1
     L.vggt_attn_plan_destroy(None)
     assert L.vggt_attn_counts(p.handle, None, None, None, None) == 0
+
+
+def test_sized_entry_points_match_the_plan(va):
+    """A LOG_SIZE plan refuses the plain forward/pack and a plain plan refuses the sized ones;
+    both checks come before any pointer is used, so they run without a GPU."""
+    L = va.lib()
+    sized = va.Plan(4, 8, 8, 2, sigma=4, diag=True, log_size=True)
+    plain = va.Plan(4, 8, 8, 2, sigma=4, diag=True)
+    assert L.vggt_attn_forward(sized.handle, None, None, None, None, None, 0, None) == -1
+    assert b"_sized" in L.vggt_attn_last_error()
+    assert L.vggt_attn_pack(sized.handle, None, None, None, 0, None) == -1
+    assert L.vggt_attn_forward_sized(plain.handle, None, None, None, None, None, None, 0, None) == -1
+    assert b"LOG_SIZE" in L.vggt_attn_last_error()
+    assert L.vggt_attn_pack_sized(sized.handle, None, None, None, None, 0, None) == -1  # log_g NULL
+    assert L.vggt_attn_pack_sized(sized.handle, None, None, 2, None, 0, None) == -4  # misaligned log_g

@@ -6,7 +6,7 @@ Workloads: dense 32 frames (and G2M on the same tensors); SGA sigma 4 at 100 fra
 COUNT means); G2F, SGA sigma 9, and sigma 9 with the phase-shifted grid and a global COUNT
 mean on the same 200-frame tensors; SGA sigma 6 at 800 frames, with and without the phase
 shift.  All use 37x37 patches + 5 special tokens per frame, 16 heads, d = 64, bf16 inputs and
-fp32 output."""
+fp32 output.  The last one gives every token a seeded group size of 1..4 (size-aware keys)."""
 import numpy as np
 import pytest
 
@@ -28,6 +28,7 @@ FULL = [
                                           phase_shift=True, mean_global=True)),
     ("sga6-800f", Desc(800, 37, 37, 16, sigma=6, diag=True, mean=True)),
     ("sga6-800f-phase", Desc(800, 37, 37, 16, sigma=6, diag=True, mean=True, phase_shift=True)),
+    ("sga6-800f-sized", Desc(800, 37, 37, 16, sigma=6, diag=True, log_size=True)),
 ]
 
 _cache = {}
@@ -57,7 +58,13 @@ def test_full_size_sampled_rows(name, desc):
     out = plan.new_output()
     ws = plan.new_workspace()
     print(f"[full] {name}: pack + attend", flush=True)
-    plan.pack(kd, vd, ws)
+    log_g = None
+    if desc.log_size:
+        from synth import make_log_sizes
+        _, log_g = make_log_sizes(desc.frames, desc.grid_h, desc.grid_w, desc.n_special, seed=5)
+        plan.pack_sized(kd, vd, torch.from_numpy(log_g).cuda(), ws)
+    else:
+        plan.pack(kd, vd, ws)
     plan.attend(qd, kd, vd, out, ws)
     torch.cuda.synchronize()
     assert bool(torch.isfinite(out).all())
@@ -69,6 +76,6 @@ def test_full_size_sampled_rows(name, desc):
     got = out[:, torch.from_numpy(rows).cuda()].double().cpu().numpy()
     del out, ws
     print(f"[full] {name}: oracle on {rows.size} rows", flush=True)
-    ref = oracle.attention(q, k, v, desc, rows=rows, workers=host_threads())
+    ref = oracle.attention(q, k, v, desc, rows=rows, workers=host_threads(), log_g=log_g)
     print(f"[full] {name}: max-abs %.3e rel-L2 %.3e" % errors(got, ref), flush=True)
     assert_close(got, ref, fp32=False, label=name)

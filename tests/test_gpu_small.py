@@ -274,3 +274,57 @@ def test_parity_prescaled_q(lib, desc, label):
     torch.cuda.synchronize()
     ref = oracle.attention(q, k, v, desc, workers=4)
     assert_close(out.float().cpu().numpy(), ref, fp32=False, label=label + "/prescaled")
+
+
+SIZED = [
+    (Desc(3, 5, 7, 2, sigma=1, log_size=True), "dense-tiny-sized"),
+    (Desc(6, 13, 11, 2, sigma=6, diag=True, log_size=True), "sga6-diag-sized"),
+    (Desc(5, 13, 11, 3, g2f=True, log_size=True), "g2f-sized"),
+    (Desc(7, 37, 37, 2, sigma=4, diag=True, phase_shift=True, log_size=True), "sga4-phase-diag-sized-37x37"),
+    (Desc(3, 37, 37, 2, sigma=1, log_size=True), "dense-sized-37x37"),
+]
+
+
+def run_sized(va, desc, q, k, v, log_g, out_dtype="fp32", in_dtype="bf16"):
+    import torch
+    plan = va.Plan(**plan_kwargs(desc, in_dtype, out_dtype))
+    out = plan.new_output()
+    plan.forward_sized(to_device(q), to_device(k), to_device(v), torch.from_numpy(log_g).cuda(), out,
+                       plan.new_workspace())
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy()
+
+
+@pytest.mark.parametrize("desc,label", SIZED, ids=[c[1] for c in SIZED])
+@pytest.mark.parametrize("out_dtype", ["fp32", "bf16"])
+def test_parity_log_size(lib, desc, label, out_dtype):
+    """Size-aware keys (+ log g on each token key's logit) with seeded group sizes 1..4."""
+    from synth import make_log_sizes
+    print(f"[sized] {label} {out_dtype}", flush=True)
+    q, k, v = inputs_for(desc, "bf16", seed=zlib.crc32(label.encode()) % 1000)
+    _, lg = make_log_sizes(desc.frames, desc.grid_h, desc.grid_w, desc.n_special, seed=5)
+    got = run_sized(lib, desc, q, k, v, lg, out_dtype=out_dtype)
+    ref = oracle.attention(q, k, v, desc, workers=4, log_g=lg)
+    assert_close(got, ref, fp32=False, label=label + "/" + out_dtype)
+
+
+@pytest.mark.parametrize("desc,label", [(Desc(4, 8, 8, 2, sigma=4, diag=True, log_size=True), "fp32-sga4-sized"),
+                                        (Desc(3, 9, 9, 2, g2f=True, log_size=True), "fp32-g2f-sized")],
+                         ids=["fp32-sga4-sized", "fp32-g2f-sized"])
+def test_parity_log_size_fp32(lib, desc, label):
+    from synth import make_log_sizes
+    q, k, v = inputs_for(desc, "fp32", seed=9)
+    _, lg = make_log_sizes(desc.frames, desc.grid_h, desc.grid_w, desc.n_special, seed=6)
+    got = run_sized(lib, desc, q, k, v, lg, in_dtype="fp32")
+    ref = oracle.attention(q, k, v, desc, log_g=lg)
+    assert_close(got, ref, fp32=True, label=label)
+
+
+def test_log_size_zero_sizes_equal_plain_path(lib):
+    """log g = 0 everywhere: the size-aware kernel must give the plain kernel's bits."""
+    desc = Desc(6, 13, 11, 2, sigma=6, diag=True, log_size=True)
+    plain = Desc(6, 13, 11, 2, sigma=6, diag=True)
+    q, k, v = inputs_for(desc, "bf16", seed=10)
+    got = run_sized(lib, desc, q, k, v, np.zeros(desc.T, dtype=np.float32))
+    _, ref, _, _ = run(lib, plain, q, k, v)
+    assert np.array_equal(got, ref)

@@ -14,13 +14,13 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libvggt_att
 
 BF16, FP32 = 0, 1
 G2F, REF_DENSE, DIAG, MEAN, MEAN_COUNT, PRESCALE_Q = 1, 2, 4, 8, 16, 32
-PHASE_SHIFT, MEAN_GLOBAL, G2M = 64, 128, 256
+PHASE_SHIFT, MEAN_GLOBAL, G2M, LOG_SIZE = 64, 128, 256, 512
 
 STATUS = {0: "OK", -1: "EINVAL", -2: "EUNSUPPORTED", -3: "ENOSPC", -4: "EALIGN", -5: "EALIAS", -6: "EHIP"}
 
 EXPORTS = ("vggt_attn_plan", "vggt_attn_plan_destroy", "vggt_attn_workspace_bytes", "vggt_attn_counts",
            "vggt_attn_layout", "vggt_attn_forward", "vggt_attn_pack", "vggt_attn_attend",
-           "vggt_attn_copy_index_set", "vggt_attn_last_error")
+           "vggt_attn_forward_sized", "vggt_attn_pack_sized", "vggt_attn_copy_index_set", "vggt_attn_last_error")
 
 
 class VggtAttnError(RuntimeError):
@@ -33,7 +33,7 @@ class VggtAttnError(RuntimeError):
 class Layout(ctypes.Structure):
     _fields_ = [(name, ctypes.c_int64) for name in (
         "segments", "segment_rows", "keys_per_segment", "off_index", "off_dcount", "off_means",
-        "off_partial", "off_kpack", "off_vpack", "total_bytes")]
+        "off_partial", "off_kbias", "off_logsize", "off_kpack", "off_vpack", "total_bytes")]
 
     def as_dict(self) -> dict:
         return {name: int(getattr(self, name)) for name, _ in self._fields_}
@@ -67,6 +67,10 @@ def lib() -> ctypes.CDLL:
     L.vggt_attn_pack.restype = ctypes.c_int
     L.vggt_attn_attend.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     L.vggt_attn_attend.restype = ctypes.c_int
+    L.vggt_attn_forward_sized.argtypes = [vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    L.vggt_attn_forward_sized.restype = ctypes.c_int
+    L.vggt_attn_pack_sized.argtypes = [vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    L.vggt_attn_pack_sized.restype = ctypes.c_int
     L.vggt_attn_copy_index_set.argtypes = [vp, vp, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32), vp]
     L.vggt_attn_copy_index_set.restype = ctypes.c_int
     L.vggt_attn_last_error.argtypes = []
@@ -109,12 +113,12 @@ class Plan:
                  mean: bool = False, mean_count: bool = False, g2f: bool = False,
                  in_dtype: str = "bf16", out_dtype: str = "fp32", prescale_q: bool = False,
                  phase_shift: bool = False, mean_global: bool = False, g2m: bool = False,
-                 flags: int | None = None):
+                 log_size: bool = False, flags: int | None = None):
         if flags is None:
             flags = ((G2F if g2f else 0) | (REF_DENSE if ref_dense else 0) | (DIAG if diag else 0) |
                      (MEAN if mean else 0) | (MEAN_COUNT if mean_count else 0) |
                      (PRESCALE_Q if prescale_q else 0) | (PHASE_SHIFT if phase_shift else 0) |
-                     (MEAN_GLOBAL if mean_global else 0) | (G2M if g2m else 0))
+                     (MEAN_GLOBAL if mean_global else 0) | (G2M if g2m else 0) | (LOG_SIZE if log_size else 0))
         self._h = ctypes.c_void_p()
         self.frames, self.grid_h, self.grid_w, self.heads, self.head_dim = frames, grid_h, grid_w, heads, head_dim
         self.n_special, self.sigma, self.flags = n_special, sigma, flags
@@ -184,6 +188,32 @@ class Plan:
                                        workspace.numel() * workspace.element_size(),
                                        _stream_handle(stream, q.device)))
 
+    def _check_log_g(self, log_g) -> None:
+        import torch
+        if log_g is None:
+            raise ValueError("this plan has LOG_SIZE: pass log_g")
+        if not log_g.is_cuda or log_g.dtype != torch.float32 or tuple(log_g.shape) != (self.T,) \
+                or not log_g.is_contiguous():
+            raise ValueError(f"log_g must be a contiguous float32 GPU tensor of shape [{self.T}]")
+
+    def forward_sized(self, q, k, v, log_g, out, workspace, stream=None) -> None:
+        for t, n in ((q, "q"), (k, "k"), (v, "v")):
+            self._check_tensor(t, n, self.in_dtype)
+        self._check_tensor(out, "out", self.out_dtype)
+        self._check_ws(workspace)
+        self._check_log_g(log_g)
+        _check(lib().vggt_attn_forward_sized(self._h, _ptr(q), _ptr(k), _ptr(v), _ptr(log_g), _ptr(out),
+                                             _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                             _stream_handle(stream, q.device)))
+
+    def pack_sized(self, k, v, log_g, workspace, stream=None) -> None:
+        for t, n in ((k, "k"), (v, "v")):
+            self._check_tensor(t, n, self.in_dtype)
+        self._check_ws(workspace)
+        self._check_log_g(log_g)
+        _check(lib().vggt_attn_pack_sized(self._h, _ptr(k), _ptr(v), _ptr(log_g), _ptr(workspace),
+                                          workspace.numel() * workspace.element_size(), _stream_handle(stream, k.device)))
+
     def pack(self, k, v, workspace, stream=None) -> None:
         for t, n in ((k, "k"), (v, "v")):
             self._check_tensor(t, n, self.in_dtype)
@@ -213,9 +243,12 @@ class Plan:
         return idx, dcount
 
 
-def attention(q, k, v, plan: Plan, stream=None):
+def attention(q, k, v, plan: Plan, stream=None, log_g=None):
     """Allocate out and a workspace with torch, run one forward, return out."""
     out = plan.new_output(q.device)
     ws = plan.new_workspace(q.device)
-    plan.forward(q, k, v, out, ws, stream)
+    if plan.flags & LOG_SIZE:
+        plan.forward_sized(q, k, v, log_g, out, ws, stream)
+    else:
+        plan.forward(q, k, v, out, ws, stream)
     return out

@@ -67,6 +67,9 @@ struct AttnArgs {
   float mean_bias_s[kMaxPhases];     // raw-score units, ln(n)/tau (0 for UNIT weighting)
   float mean_bias_log2[kMaxPhases];  // the same in log2 units, log2(n) (PRESCALE_Q path)
   float c_log2;    // tau * log2(e)
+  const float* kbias;    // size-aware keys: bias of each packed key row (raw-score units), else null
+  const float* logsize;  // size-aware keys: log g per token (for the diagonal term), else null
+  float size_scale;      // sqrt(d): log g -> raw-score units
   int qtiles;      // query tiles per head
   int g2f;
   int qtiles_per_frame;
@@ -100,9 +103,10 @@ __device__ __forceinline__ float group_sum(float x) {
   return __uint_as_float(q[0]) + __uint_as_float(q[1]);
 }
 
-template <int QB, int WPE, bool OUT_BF16, bool PRESCALE_Q>
+template <int QB, int WPE, bool OUT_BF16, bool PRESCALE_Q, bool LOGSIZE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 void attn_bf16_kernel(AttnArgs a) {
+  static_assert(!(LOGSIZE && PRESCALE_Q), "size-aware keys use the exact scale");
   constexpr bool kExactScale = !PRESCALE_Q;
   constexpr int WQ = 16 * QB;  // query rows per wave
   constexpr int BM = 4 * WQ;   // query rows per work-group
@@ -116,8 +120,12 @@ void attn_bf16_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t kbuf1[kTile * 128];
   __shared__ __attribute__((aligned(16))) uint8_t vbuf0[kTile * 128];
   __shared__ __attribute__((aligned(16))) uint8_t vbuf1[kTile * 128];
+  // Size-aware keys: the 64 key biases of a K tile travel with it (same schedule, same parity).
+  __shared__ __attribute__((aligned(16))) float bbuf0[kTile];
+  __shared__ __attribute__((aligned(16))) float bbuf1[kTile];
   auto kbuf = [&](auto par) -> uint8_t* { if constexpr (decltype(par)::value == 0) return kbuf0; else return kbuf1; };
   auto vbuf = [&](auto par) -> uint8_t* { if constexpr (decltype(par)::value == 0) return vbuf0; else return vbuf1; };
+  auto bbuf = [&](auto par) -> float* { if constexpr (decltype(par)::value == 0) return bbuf0; else return bbuf1; };
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, grp = lane >> 4;
@@ -142,6 +150,7 @@ void attn_bf16_kernel(AttnArgs a) {
   const size_t seg_off = (size_t(h) * a.rows_per_head + size_t(seg) * a.segment_rows) * kHeadDim;
   const uint16_t* kseg = static_cast<const uint16_t*>(a.kpack) + seg_off;
   const uint16_t* vseg = static_cast<const uint16_t*>(a.vpack) + seg_off;
+  const float* bseg = LOGSIZE ? a.kbias + size_t(seg) * a.segment_rows : nullptr;
 
   // Q as the B operand of S^T = K Q^T: lane (l16, grp) holds query l16 of its block and
   // channels cc*32 + grp*8 .. +7 for cc = 0, 1.
@@ -184,6 +193,9 @@ void attn_bf16_kernel(AttnArgs a) {
     // Diagonal term: a query whose own token is not in S starts with its self term
     // (m = self logit, l = 1, O = v_self); the others start empty.
     dot = group_sum(dot);
+    if constexpr (LOGSIZE) {
+      if (self) dot += a.logsize[t] * a.size_scale;
+    }
     m_run[qb] = self ? dot : -INFINITY;
     l_run[qb] = (self && grp == 0) ? 1.f : 0.f;
 #pragma unroll
@@ -216,6 +228,16 @@ void attn_bf16_kernel(AttnArgs a) {
           (__attribute__((address_space(3))) void*)(buf + blk * 1024), 16, 0, 0);
     }
   };
+  // Key biases of tile j: wave 0 copies the 64 floats with 4-byte global->LDS loads (lane L
+  // lands at LDS base + 4*L).
+  auto async_bias = [&](int j, float* buf) {
+    if constexpr (LOGSIZE) {
+      if (wave == 0)
+        __builtin_amdgcn_global_load_lds(
+            (__attribute__((address_space(1))) void*)(bseg + size_t(j) * kTile + lane),
+            (__attribute__((address_space(3))) void*)buf, 4, 0, 0);
+    }
+  };
   auto wait_tiles = [&]() { __builtin_amdgcn_s_waitcnt(kWaitVmcnt0); };
   // 16-byte operand read of LDS row `row`, chunk `ch` (undoing the swizzle).
   auto lds_frag = [&](const uint8_t* buf, int row, int ch) {
@@ -235,12 +257,14 @@ void attn_bf16_kernel(AttnArgs a) {
   // first MFMA reads no accumulator registers and the second takes its input straight from the
   // first); the running max is applied in the exp argument.  PRESCALE_Q mode starts it from
   // -m, so the scores leave the matrix core already shifted.
-  auto scores_qb = [&](const bf16x8_t (&kf)[4][2], int qb, f32x4_t (&s)[4]) {
+  // Size-aware keys start the chain from the keys' biases instead (read from LDS).
+  auto scores_qb = [&](const bf16x8_t (&kf)[4][2], const float* bb, int qb, f32x4_t (&s)[4]) {
     const float mneg = -m_run[qb];
 #pragma unroll
     for (int k4 = 0; k4 < 4; ++k4) {
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
       if constexpr (PRESCALE_Q) acc = f32x4_t{mneg, mneg, mneg, mneg};
+      if constexpr (LOGSIZE) acc = *reinterpret_cast<const f32x4_t*>(bb + k4 * 16 + grp * 4);
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[k4][0], qf[qb][0], acc, 0, 0, 0);
       s[k4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[k4][1], qf[qb][1], acc, 0, 0, 0);
     }
@@ -310,9 +334,9 @@ void attn_bf16_kernel(AttnArgs a) {
   // the matrix cores in the same stretch of code.  Lazy running max: weights are taken against
   // the current m; only if some weight reaches 2 is m raised exactly to the row max (O and l
   // rescaled) and the block redone, so in the steady state no per-score max and no rescale run.
-  auto block = [&](const bf16x8_t (&kf)[4][2], int qb, f32x4_t (&s_cur)[4], f32x4_t (&s_next)[4],
-                   bf16x8_t (&pf)[2], bool next) {
-    if (next) scores_qb(kf, qb, s_next);
+  auto block = [&](const bf16x8_t (&kf)[4][2], const float* bb, int qb, f32x4_t (&s_cur)[4],
+                   f32x4_t (&s_next)[4], bf16x8_t (&pf)[2], bool next) {
+    if (next) scores_qb(kf, bb, qb, s_next);
     const float l_prev = l_run[qb];
     const uint32_t bits = probs_qb(qb, s_cur, pf);
     if (__builtin_amdgcn_ballot_w64((bits & 0x40004000u) != 0) != 0) {
@@ -338,8 +362,12 @@ void attn_bf16_kernel(AttnArgs a) {
 
   const int nkt = a.nktiles;
   async_tile(kseg, 0, kbuf0);
+  async_bias(0, bbuf0);
   async_tile(vseg, 0, vbuf0);
-  if (nkt > 1) async_tile(kseg, 1, kbuf1);
+  if (nkt > 1) {
+    async_tile(kseg, 1, kbuf1);
+    async_bias(1, bbuf1);
+  }
   wait_tiles();
   __syncthreads();
 
@@ -353,6 +381,7 @@ void attn_bf16_kernel(AttnArgs a) {
     using same_t = std::integral_constant<int, P>;
     using other_t = std::integral_constant<int, P ^ 1>;
     async_tile(kseg, min(j + 2, nkt - 1), kbuf(same_t{}));
+    async_bias(min(j + 2, nkt - 1), bbuf(same_t{}));
     async_tile(vseg, j + 1, vbuf(other_t{}));
     bf16x8_t kf[4][2], vf[4][2];
     k_frags(kbuf(other_t{}), kf);
@@ -360,7 +389,7 @@ void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       bf16x8_t pf[2];
-      block(kf, qb, s_cur[qb], s_next[qb], pf, true);
+      block(kf, bbuf(other_t{}), qb, s_cur[qb], s_next[qb], pf, true);
       accumulate_qb(vf, qb, pf);
     }
     if constexpr (decltype(mask_tag)::value) bias_mask(j + 1, s_next);
@@ -373,7 +402,7 @@ void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       bf16x8_t pf[2];
-      block(kf, qb, s_cur[qb], s_cur[qb], pf, false);
+      block(kf, nullptr, qb, s_cur[qb], s_cur[qb], pf, false);
       accumulate_qb(vf, qb, pf);
     }
   };
@@ -391,7 +420,7 @@ void attn_bf16_kernel(AttnArgs a) {
     for (int qb = 0; qb < QB; ++qb) {
       const float m_self = m_run[qb];
       m_run[qb] = 0.f;
-      scores_qb(kf, qb, sa[qb]);
+      scores_qb(kf, bbuf0, qb, sa[qb]);
       m_run[qb] = m_self;
     }
   }
@@ -472,6 +501,7 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
   const size_t seg_off = (size_t(h) * a.rows_per_head + size_t(seg) * a.segment_rows) * kHeadDim;
   const float* kseg = static_cast<const float*>(a.kpack) + seg_off;
   const float* vseg = static_cast<const float*>(a.vpack) + seg_off;
+  const float* bseg = a.kbias ? a.kbias + size_t(seg) * a.segment_rows : nullptr;
 
   float q[kHeadDim], o[kHeadDim];
 #pragma unroll
@@ -483,6 +513,7 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
     float dot = 0.f;
 #pragma unroll
     for (int d = 0; d < kHeadDim; ++d) dot = fmaf(q[d], Kin[size_t(t) * kHeadDim + d], dot);
+    if (a.logsize) dot += a.logsize[t] * a.size_scale;
     m_run = dot * c;
     l_run = 1.f;
   }
@@ -508,6 +539,7 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
       const int key = j * kTile + kk;
       if (key >= a.nkeys) dot = -INFINITY;
       else if (key >= a.n_plain) dot += mean_bias(a, a.mean_bias_s, key - a.n_plain);
+      else if (bseg) dot += bseg[key];
       sc[kk] = dot;
       mx = fmaxf(mx, dot);
     }
@@ -574,6 +606,11 @@ hipError_t launch_attend(const vggt_attn_plan_s& p, const void* q, const void* k
     a.mean_bias_log2[s] = float(b * tau * 1.4426950408889634);
   }
   a.c_log2 = float(tau * 1.4426950408889634);
+  if (p.log_size) {
+    a.kbias = reinterpret_cast<const float*>(base + p.layout.off_kbias);
+    a.logsize = reinterpret_cast<const float*>(base + p.layout.off_logsize);
+    a.size_scale = float(std::sqrt(double(p.head_dim)));
+  }
   a.g2f = p.g2f ? 1 : 0;
   a.diag = p.diag ? 1 : 0;
   a.g = p.geom;
@@ -605,13 +642,16 @@ hipError_t launch_attend(const vggt_attn_plan_s& p, const void* q, const void* k
   }
   const unsigned blocks = unsigned(int64_t(a.qtiles) * p.heads);
   const bool ob = p.out_dtype == VGGT_ATTN_BF16;
-  const bool pre = p.prescale_q;
+  const bool pre = p.prescale_q;  // never set together with log_size
+  const bool sz = p.log_size;
 #define VGGT_LAUNCH(QB_, WPE_)                                                                       \
   do {                                                                                              \
-    if (ob && pre) hipLaunchKernelGGL((attn_bf16_kernel<QB_, WPE_, true, true>), dim3(blocks), dim3(256), 0, stream, a);    \
-    else if (ob) hipLaunchKernelGGL((attn_bf16_kernel<QB_, WPE_, true, false>), dim3(blocks), dim3(256), 0, stream, a);     \
-    else if (pre) hipLaunchKernelGGL((attn_bf16_kernel<QB_, WPE_, false, true>), dim3(blocks), dim3(256), 0, stream, a);    \
-    else hipLaunchKernelGGL((attn_bf16_kernel<QB_, WPE_, false, false>), dim3(blocks), dim3(256), 0, stream, a);            \
+    if (sz && ob) hipLaunchKernelGGL((attn_bf16_kernel<QB_, WPE_, true, false, true>), dim3(blocks), dim3(256), 0, stream, a);  \
+    else if (sz) hipLaunchKernelGGL((attn_bf16_kernel<QB_, WPE_, false, false, true>), dim3(blocks), dim3(256), 0, stream, a); \
+    else if (ob && pre) hipLaunchKernelGGL((attn_bf16_kernel<QB_, WPE_, true, true, false>), dim3(blocks), dim3(256), 0, stream, a); \
+    else if (ob) hipLaunchKernelGGL((attn_bf16_kernel<QB_, WPE_, true, false, false>), dim3(blocks), dim3(256), 0, stream, a);  \
+    else if (pre) hipLaunchKernelGGL((attn_bf16_kernel<QB_, WPE_, false, true, false>), dim3(blocks), dim3(256), 0, stream, a); \
+    else hipLaunchKernelGGL((attn_bf16_kernel<QB_, WPE_, false, false, false>), dim3(blocks), dim3(256), 0, stream, a);        \
   } while (0)
   if (p.g2f) VGGT_LAUNCH(QBf, WPEf);
   else VGGT_LAUNCH(QBg, WPEg);

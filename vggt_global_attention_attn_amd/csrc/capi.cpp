@@ -65,12 +65,63 @@ int check_out_alias(const vggt_attn_plan_s& p, const void* q, const void* k, con
   return VGGT_ATTN_OK;
 }
 
-int do_pack(const vggt_attn_plan_s& p, const void* k, const void* v, void* ws, hipStream_t s) {
+int do_pack(const vggt_attn_plan_s& p, const void* k, const void* v, const float* log_g, void* ws,
+            hipStream_t s) {
   hipError_t e = vggt::launch_means(p, k, v, ws, s);
   if (e != hipSuccess) return hip_error(e, "means kernel launch");
   e = vggt::launch_pack(p, k, v, ws, s);
   if (e != hipSuccess) return hip_error(e, "pack kernel launch");
+  if (p.log_size) {
+    e = vggt::launch_size_bias(p, log_g, ws, s);
+    if (e != hipSuccess) return hip_error(e, "size bias kernel launch");
+  }
   return VGGT_ATTN_OK;
+}
+
+// log_g of a LOG_SIZE plan: present, 4-byte aligned, not overlapping `out` or the workspace.
+int check_log_g(const vggt_attn_plan_s& p, const float* log_g, const void* out, const void* ws,
+                size_t ws_bytes) {
+  if (!p.log_size) return set_error(VGGT_ATTN_EINVAL, "plan has no LOG_SIZE flag: use the plain entry points");
+  if (!log_g) return set_error(VGGT_ATTN_EINVAL, "log_g is NULL");
+  if (reinterpret_cast<uintptr_t>(log_g) & 3u) return set_error(VGGT_ATTN_EALIGN, "log_g is not 4-byte aligned");
+  const size_t n = size_t(p.T) * 4;
+  if (overlaps(log_g, n, ws, ws_bytes) || (out && overlaps(log_g, n, out, tensor_bytes(p, p.out_dtype))))
+    return set_error(VGGT_ATTN_EALIAS, "log_g overlaps out or the workspace");
+  return VGGT_ATTN_OK;
+}
+
+int no_log_size(const vggt_attn_plan_s& p) {
+  if (p.log_size) return set_error(VGGT_ATTN_EINVAL, "plan has LOG_SIZE: use the *_sized entry points");
+  return VGGT_ATTN_OK;
+}
+
+int pack_impl(const vggt_attn_plan_s& p, const void* k, const void* v, const float* log_g, void* workspace,
+              size_t workspace_bytes, void* stream) {
+  int rc = check_tensors(p, nullptr, k, v, nullptr, false);
+  if (rc) return rc;
+  if ((rc = check_workspace(p, workspace, workspace_bytes))) return rc;
+  const size_t nin = tensor_bytes(p, p.in_dtype);
+  if (overlaps(workspace, workspace_bytes, k, nin) || overlaps(workspace, workspace_bytes, v, nin))
+    return set_error(VGGT_ATTN_EALIAS, "workspace overlaps k or v");
+  if ((rc = do_pack(p, k, v, log_g, workspace, static_cast<hipStream_t>(stream)))) return rc;
+  return ok();
+}
+
+int forward_impl(const vggt_attn_plan_s& p, const void* q, const void* k, const void* v, const float* log_g,
+                 void* out, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_tensors(p, q, k, v, out, true);
+  if (rc) return rc;
+  if ((rc = check_workspace(p, workspace, workspace_bytes))) return rc;
+  if ((rc = check_out_alias(p, q, k, v, out, workspace, workspace_bytes))) return rc;
+  const size_t nin = tensor_bytes(p, p.in_dtype);
+  if (overlaps(workspace, workspace_bytes, k, nin) || overlaps(workspace, workspace_bytes, v, nin) ||
+      overlaps(workspace, workspace_bytes, q, nin))
+    return set_error(VGGT_ATTN_EALIAS, "workspace overlaps q, k or v");
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((rc = do_pack(p, k, v, log_g, workspace, s))) return rc;
+  hipError_t e = vggt::launch_attend(p, q, k, v, out, workspace, s);
+  if (e != hipSuccess) return hip_error(e, "attention kernel launch");
+  return ok();
 }
 
 }  // namespace
@@ -120,14 +171,15 @@ int vggt_attn_layout(const vggt_attn_plan_t* plan, vggt_attn_layout_t* out) {
 int vggt_attn_pack(const vggt_attn_plan_t* plan, const void* k, const void* v, void* workspace,
                    size_t workspace_bytes, void* stream) {
   if (!plan) return set_error(VGGT_ATTN_EINVAL, "plan is NULL");
-  int rc = check_tensors(*plan, nullptr, k, v, nullptr, false);
-  if (rc) return rc;
-  if ((rc = check_workspace(*plan, workspace, workspace_bytes))) return rc;
-  const size_t nin = tensor_bytes(*plan, plan->in_dtype);
-  if (overlaps(workspace, workspace_bytes, k, nin) || overlaps(workspace, workspace_bytes, v, nin))
-    return set_error(VGGT_ATTN_EALIAS, "workspace overlaps k or v");
-  if ((rc = do_pack(*plan, k, v, workspace, static_cast<hipStream_t>(stream)))) return rc;
-  return ok();
+  if (int rc = no_log_size(*plan)) return rc;
+  return pack_impl(*plan, k, v, nullptr, workspace, workspace_bytes, stream);
+}
+
+int vggt_attn_pack_sized(const vggt_attn_plan_t* plan, const void* k, const void* v, const float* log_g,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  if (!plan) return set_error(VGGT_ATTN_EINVAL, "plan is NULL");
+  if (int rc = check_log_g(*plan, log_g, nullptr, workspace, workspace_bytes)) return rc;
+  return pack_impl(*plan, k, v, log_g, workspace, workspace_bytes, stream);
 }
 
 int vggt_attn_attend(const vggt_attn_plan_t* plan, const void* q, const void* k, const void* v,
@@ -145,19 +197,16 @@ int vggt_attn_attend(const vggt_attn_plan_t* plan, const void* q, const void* k,
 int vggt_attn_forward(const vggt_attn_plan_t* plan, const void* q, const void* k, const void* v,
                       void* out, void* workspace, size_t workspace_bytes, void* stream) {
   if (!plan) return set_error(VGGT_ATTN_EINVAL, "plan is NULL");
-  int rc = check_tensors(*plan, q, k, v, out, true);
-  if (rc) return rc;
-  if ((rc = check_workspace(*plan, workspace, workspace_bytes))) return rc;
-  if ((rc = check_out_alias(*plan, q, k, v, out, workspace, workspace_bytes))) return rc;
-  const size_t nin = tensor_bytes(*plan, plan->in_dtype);
-  if (overlaps(workspace, workspace_bytes, k, nin) || overlaps(workspace, workspace_bytes, v, nin) ||
-      overlaps(workspace, workspace_bytes, q, nin))
-    return set_error(VGGT_ATTN_EALIAS, "workspace overlaps q, k or v");
-  const hipStream_t s = static_cast<hipStream_t>(stream);
-  if ((rc = do_pack(*plan, k, v, workspace, s))) return rc;
-  hipError_t e = vggt::launch_attend(*plan, q, k, v, out, workspace, s);
-  if (e != hipSuccess) return hip_error(e, "attention kernel launch");
-  return ok();
+  if (int rc = no_log_size(*plan)) return rc;
+  return forward_impl(*plan, q, k, v, nullptr, out, workspace, workspace_bytes, stream);
+}
+
+int vggt_attn_forward_sized(const vggt_attn_plan_t* plan, const void* q, const void* k, const void* v,
+                            const float* log_g, void* out, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  if (!plan) return set_error(VGGT_ATTN_EINVAL, "plan is NULL");
+  if (int rc = check_log_g(*plan, log_g, out, workspace, workspace_bytes)) return rc;
+  return forward_impl(*plan, q, k, v, log_g, out, workspace, workspace_bytes, stream);
 }
 
 int vggt_attn_copy_index_set(const vggt_attn_plan_t* plan, const void* workspace,

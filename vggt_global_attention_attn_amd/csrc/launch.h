@@ -16,6 +16,9 @@ hipError_t launch_means(const vggt_attn_plan_s& p, const void* k, const void* v,
 hipError_t launch_pack(const vggt_attn_plan_s& p, const void* k, const void* v, void* ws,
                        hipStream_t stream);
 
+// LOG_SIZE plans: packed per-key logit bias and a copy of log_g -> workspace.
+hipError_t launch_size_bias(const vggt_attn_plan_s& p, const float* log_g, void* ws, hipStream_t stream);
+
 // Attention over the packed keys (bf16 inputs: MFMA kernel; fp32 inputs: fp32 kernel).
 hipError_t launch_attend(const vggt_attn_plan_s& p, const void* q, const void* k, const void* v,
                          void* out, const void* ws, hipStream_t stream);

@@ -19,7 +19,13 @@
 //                        key-minor tiles in the order the PV matrix-core step reads them, so
 //                        the attention kernel loads every operand with contiguous 16-byte
 //                        reads.  Head 0 also exports S, and work-group (0,0) exports |D_f|.
+//   size_bias_kernel     size-aware keys ("RegimeVGGT" notes, 关键设计 2): the logit bias of
+//                        every packed key row, log g of its token in raw-score units, and a
+//                        copy of log g for the diagonal term.
 #include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
 
 #include "device_common.h"
 #include "launch.h"
@@ -219,7 +225,45 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a) {
   }
 }
 
+struct SizeBiasArgs {
+  PackArgs pk;           // geometry of the packed rows (packed_source)
+  const float* log_g;    // [T]
+  float* kbias;          // [segments * segment_rows]
+  float* logsize;        // [T]
+  int64_t rows;          // segments * segment_rows
+  float scale;           // sqrt(d) = 1 / tau: logit units -> raw-score units
+};
+
+__global__ __launch_bounds__(256) void size_bias_kernel(SizeBiasArgs a) {
+  const int64_t stride = int64_t(gridDim.x) * 256;
+  for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < a.rows; i += stride) {
+    const int64_t src = packed_source(a.pk, i);
+    a.kbias[i] = src >= 0 ? a.log_g[src] * a.scale : 0.f;  // padding rows are masked later
+  }
+  for (int64_t t = int64_t(blockIdx.x) * 256 + threadIdx.x; t < a.pk.T; t += stride) a.logsize[t] = a.log_g[t];
+}
+
 }  // namespace
+
+hipError_t launch_size_bias(const vggt_attn_plan_s& p, const float* log_g, void* ws, hipStream_t stream) {
+  char* base = static_cast<char*>(ws);
+  SizeBiasArgs a{};
+  a.pk.T = p.T;
+  a.pk.nS = p.nS;
+  a.pk.M = int(p.M);
+  a.pk.g2f = p.g2f ? 1 : 0;
+  a.pk.segment_rows = int(p.segment_rows);
+  a.pk.g = p.geom;
+  a.log_g = log_g;
+  a.kbias = reinterpret_cast<float*>(base + p.layout.off_kbias);
+  a.logsize = reinterpret_cast<float*>(base + p.layout.off_logsize);
+  a.rows = p.rows_per_head;
+  a.scale = float(std::sqrt(double(p.head_dim)));
+  const int64_t work = a.rows > p.T ? a.rows : p.T;
+  const unsigned blocks = unsigned(std::min<int64_t>((work + 255) / 256, 4096));
+  hipLaunchKernelGGL(size_bias_kernel, dim3(blocks), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_means(const vggt_attn_plan_s& p, const void* k, const void* v, void* ws,
                         hipStream_t stream) {

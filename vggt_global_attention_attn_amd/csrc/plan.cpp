@@ -53,7 +53,7 @@ int build_plan(vggt_attn_plan_s* p, int frames, int grid_h, int grid_w, int n_sp
     return fail(err, VGGT_ATTN_EINVAL, "sigma %lld not in {1, 2, 4, 6, 9}", sigma);
   const unsigned known = VGGT_ATTN_G2F | VGGT_ATTN_REF_DENSE | VGGT_ATTN_DIAG | VGGT_ATTN_MEAN |
                          VGGT_ATTN_MEAN_COUNT | VGGT_ATTN_PRESCALE_Q | VGGT_ATTN_PHASE_SHIFT |
-                         VGGT_ATTN_MEAN_GLOBAL | VGGT_ATTN_G2M;
+                         VGGT_ATTN_MEAN_GLOBAL | VGGT_ATTN_G2M | VGGT_ATTN_LOG_SIZE;
   if (flags & ~known) return fail(err, VGGT_ATTN_EINVAL, "unknown flag bits 0x%llx", flags & ~known);
   const bool g2f = flags & VGGT_ATTN_G2F;
   const bool g2m = flags & VGGT_ATTN_G2M;
@@ -64,6 +64,8 @@ int build_plan(vggt_attn_plan_s* p, int frames, int grid_h, int grid_w, int n_sp
     return fail(err, VGGT_ATTN_EINVAL, "G2M takes sigma == 1 and none of DIAG/MEAN/MEAN_GLOBAL/PHASE_SHIFT");
   if ((flags & VGGT_ATTN_MEAN_GLOBAL) && !(flags & VGGT_ATTN_MEAN))
     return fail(err, VGGT_ATTN_EINVAL, "MEAN_GLOBAL requires MEAN");
+  if ((flags & VGGT_ATTN_LOG_SIZE) && (flags & (VGGT_ATTN_MEAN | VGGT_ATTN_G2M)))
+    return fail(err, VGGT_ATTN_EINVAL, "LOG_SIZE is not combined with MEAN or G2M");
   const bool dtype_ok = (in_dtype == VGGT_ATTN_BF16 && (out_dtype == VGGT_ATTN_FP32 || out_dtype == VGGT_ATTN_BF16)) ||
                         (in_dtype == VGGT_ATTN_FP32 && out_dtype == VGGT_ATTN_FP32);
   if (!dtype_ok)
@@ -87,7 +89,8 @@ int build_plan(vggt_attn_plan_s* p, int frames, int grid_h, int grid_w, int n_sp
   p->mean = (flags & VGGT_ATTN_MEAN) && p->subsampled;
   p->mean_global = (flags & VGGT_ATTN_MEAN_GLOBAL) && p->mean;
   p->mean_count = flags & VGGT_ATTN_MEAN_COUNT;
-  p->prescale_q = flags & VGGT_ATTN_PRESCALE_Q;
+  p->log_size = flags & VGGT_ATTN_LOG_SIZE;
+  p->prescale_q = (flags & VGGT_ATTN_PRESCALE_Q) && !p->log_size;
   p->phase = (flags & VGGT_ATTN_PHASE_SHIFT) && p->subsampled;
   p->s_h = s_h; p->s_w = s_w;
   p->L = int(L); p->P = int(P); p->T = T;
@@ -180,6 +183,8 @@ int build_plan(vggt_attn_plan_s* p, int frames, int grid_h, int grid_w, int n_sp
   lay.off_means = off;  off = align256(off + int64_t(heads) * p->M * 2 * head_dim * int64_t(p->elem_bytes));
   const int64_t partials = (p->mean_global || p->g2m) ? p->M_frames : 0;
   lay.off_partial = off; off = align256(off + int64_t(heads) * partials * 2 * head_dim * 4);
+  lay.off_kbias = off;  off = align256(off + (p->log_size ? p->rows_per_head * 4 : 0));
+  lay.off_logsize = off; off = align256(off + (p->log_size ? T * 4 : 0));
   lay.off_kpack = off;  off = align256(off + int64_t(heads) * p->rows_per_head * head_dim * int64_t(p->elem_bytes));
   lay.off_vpack = off;  off = align256(off + int64_t(heads) * p->rows_per_head * head_dim * int64_t(p->elem_bytes));
   lay.total_bytes = off;

@@ -49,7 +49,7 @@ struct vggt_attn_plan_s {
   int in_dtype, out_dtype;
   // derived
   bool g2f, ref_dense, diag, mean, mean_count, subsampled, prescale_q;
-  bool phase, mean_global, g2m;
+  bool phase, mean_global, g2m, log_size;
   int s_h, s_w, L, P;
   int64_t T;
   int64_t dropped_of_phase[vggt::kMaxPhases];  // |D_f| of a compressed frame of phase k
