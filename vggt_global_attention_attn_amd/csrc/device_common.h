@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <utility>
 
 #include "plan.h"
 
@@ -22,25 +23,31 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return uint32_t(f32_to_bf16(lo)) | (uint32_t(f32_to_bf16(hi)) << 16);
 }
 
-// t[i] for a run-time i, written as a chain of selects over compile-time indices: indexing an
+// t[i] for a run-time i, written as a chain of selects over compile-time indices (a fold
+// expression, so every access has a constant index before any loop pass runs): indexing an
 // array of the kernel-argument struct with a run-time value would make the compiler copy the
 // whole struct to scratch memory.
+template <typename V, int N, int... I>
+__host__ __device__ __forceinline__ V pick_impl(const V (&t)[N], int i, std::integer_sequence<int, I...>) {
+  V r = t[0];
+  ((r = (i == I) ? t[I] : r), ...);
+  return r;
+}
 template <typename V, int N>
 __host__ __device__ __forceinline__ V pick(const V (&t)[N], int i) {
-  V r = t[0];
-#pragma unroll
-  for (int j = 1; j < N; ++j) r = (i == j) ? t[j] : r;
-  return r;
+  return pick_impl(t, i, std::make_integer_sequence<int, N>{});
 }
 
 // Largest k < n with prefix[k] <= x, for a nondecreasing prefix with prefix[0] <= x: the
 // number of j in [1, n) with prefix[j] <= x.
+template <int N, int... I>
+__host__ __device__ __forceinline__ int prefix_slot_impl(const int (&prefix)[N], int n, int x,
+                                                         std::integer_sequence<int, I...>) {
+  return ((int(I > 0 && I < n) & int(prefix[I] <= x)) + ...);
+}
 template <int N>
 __host__ __device__ __forceinline__ int prefix_slot(const int (&prefix)[N], int n, int x) {
-  int k = 0;
-#pragma unroll
-  for (int j = 1; j < N; ++j) k += int(j < n) & int(prefix[j] <= x);
-  return k;
+  return prefix_slot_impl(prefix, n, x, std::make_integer_sequence<int, N>{});
 }
 
 // Grid phase of frame f: f mod (s_h*s_w) with the phase-shifted grid, else 0.  Phase k has
