@@ -157,3 +157,12 @@ def test_sized_entry_points_match_the_plan(va):
     assert b"LOG_SIZE" in L.vggt_attn_last_error()
     assert L.vggt_attn_pack_sized(sized.handle, None, None, None, None, 0, None) == -1  # log_g NULL
     assert L.vggt_attn_pack_sized(sized.handle, None, None, 2, None, 0, None) == -4  # misaligned log_g
+
+
+def test_token_limit_is_exact(va):
+    """T = frames * 1374 may reach 8,000,000: 5822 frames (7,999,428 tokens) plan, 5823 do not."""
+    p = va.Plan(5822, 37, 37, 6, g2f=True)
+    assert p.T == 7_999_428 and p.counts()["n_kv"] == 1374
+    with pytest.raises(va.VggtAttnError) as ei:
+        va.Plan(5823, 37, 37, 6, g2f=True)
+    assert ei.value.status == "EINVAL"

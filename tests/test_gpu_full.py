@@ -6,7 +6,8 @@ Workloads: dense 32 frames (and G2M on the same tensors); SGA sigma 4 at 100 fra
 COUNT means); G2F, SGA sigma 9, and sigma 9 with the phase-shifted grid and a global COUNT
 mean on the same 200-frame tensors; SGA sigma 6 at 800 frames, with and without the phase
 shift.  All use 37x37 patches + 5 special tokens per frame, 16 heads, d = 64, bf16 inputs and
-fp32 output.  The last one gives every token a seeded group size of 1..4 (size-aware keys)."""
+fp32 output.  One gives every token a seeded group size of 1..4 (size-aware keys); the last runs
+G2F at the largest token count a plan accepts."""
 import numpy as np
 import pytest
 
@@ -29,6 +30,9 @@ FULL = [
     ("sga6-800f", Desc(800, 37, 37, 16, sigma=6, diag=True, mean=True)),
     ("sga6-800f-phase", Desc(800, 37, 37, 16, sigma=6, diag=True, mean=True, phase_shift=True)),
     ("sga6-800f-sized", Desc(800, 37, 37, 16, sigma=6, diag=True, log_size=True)),
+    # the largest plan the library accepts: T = 7,999,428 tokens (limit 8,000,000); with 6 heads
+    # an [H][T][64] tensor holds 3.07e9 elements, so every offset needs 64 bits
+    ("g2f-5822f-max", Desc(5822, 37, 37, 6, g2f=True)),
 ]
 
 _cache = {}
