@@ -111,6 +111,10 @@ typedef struct {
   int64_t off_kbias;         /* float [segments*segment_rows]: logit bias of each packed key
                                 in raw-score units, log_g[t] * sqrt(d) (LOG_SIZE only)        */
   int64_t off_logsize;       /* float [T]: copy of log_g (LOG_SIZE only)                      */
+  int64_t off_part;          /* float: partial softmax states (running max, sum, unnormalised
+                                output) of the key-range pieces of a split last round of
+                                work-groups, merged before the call returns (bf16 inputs)     */
+  int64_t split_pieces;      /* key-range pieces per work item of that round (0 = no split)   */
   int64_t off_kpack;         /* [H][segments*segment_rows][d] input dtype                    */
   int64_t off_vpack;         /* bf16: [H][rows/64][d][64] key-minor tiles (see below);
                                 fp32: [H][rows][d]                                           */
@@ -171,9 +175,12 @@ int vggt_attn_pack(const vggt_attn_plan_t* plan, const void* k, const void* v, v
                    size_t workspace_bytes, void* stream);
 
 /* Attention stage on a workspace already filled by vggt_attn_pack for the same plan and the
- * same k, v (k and v are read again for the diagonal term).  Writes every element of out. */
+ * same k, v (k and v are read again for the diagonal term).  Writes every element of out.  It
+ * uses the workspace's off_part area as scratch (the partial softmax states of a split last
+ * round of work-groups, see vggt_attn_layout_t) and leaves the packed parts unchanged, so it
+ * may be called again on the same workspace. */
 int vggt_attn_attend(const vggt_attn_plan_t* plan, const void* q, const void* k, const void* v,
-                     void* out, const void* workspace, size_t workspace_bytes, void* stream);
+                     void* out, void* workspace, size_t workspace_bytes, void* stream);
 
 /* The same calls for a LOG_SIZE plan (vggt_attn_forward and vggt_attn_pack return EINVAL for
  * one, and these return EINVAL for a plan without LOG_SIZE).  log_g: device float [T], 4-byte

@@ -26,18 +26,6 @@
 #include "device_common.h"
 #include "launch.h"
 
-#ifndef VGGT_GLOBAL_QB
-#define VGGT_GLOBAL_QB 3
-#endif
-#ifndef VGGT_GLOBAL_WPE
-#define VGGT_GLOBAL_WPE 2
-#endif
-#ifndef VGGT_G2F_QB
-#define VGGT_G2F_QB 2
-#endif
-#ifndef VGGT_G2F_WPE
-#define VGGT_G2F_WPE 2
-#endif
 
 namespace vggt {
 namespace {
@@ -70,12 +58,37 @@ struct AttnArgs {
   const float* kbias;    // size-aware keys: bias of each packed key row (raw-score units), else null
   const float* logsize;  // size-aware keys: log g per token (for the diagonal term), else null
   float size_scale;      // sqrt(d): log g -> raw-score units
+  int64_t split_from;    // first work item of the split last round
+  int nsplit;            // key-range pieces per split item (1: none)
+  float* part;           // [split items * nsplit][BM][kPartRow] partial states of the pieces
   int qtiles;      // query tiles per head
   int g2f;
   int qtiles_per_frame;
   int diag;
   IndexGeom g;
 };
+
+// Query rows [row0, row_end) of a work item of BM rows, its head and its key segment.
+struct ItemRows {
+  int h;
+  int64_t row0, row_end, seg;
+};
+__device__ __forceinline__ ItemRows item_rows(const AttnArgs& a, int64_t item, int BM) {
+  ItemRows r;
+  r.h = int(item / a.qtiles);
+  const int qt = int(item - int64_t(r.h) * a.qtiles);
+  if (a.g2f) {
+    const int f = qt / a.qtiles_per_frame, qf = qt - f * a.qtiles_per_frame;
+    r.row0 = int64_t(f) * a.g.L + int64_t(qf) * BM;
+    r.row_end = int64_t(f + 1) * a.g.L;
+    r.seg = f;
+  } else {
+    r.row0 = int64_t(qt) * BM;
+    r.row_end = a.T;
+    r.seg = 0;
+  }
+  return r;
+}
 
 // Logit bias of mean key m (0 <= m < M): it depends only on the grid phase of the frame the
 // key stands for, i.e. on the key's slot within a run of phases.
@@ -103,10 +116,13 @@ __device__ __forceinline__ float group_sum(float x) {
   return __uint_as_float(q[0]) + __uint_as_float(q[1]);
 }
 
-template <int QB, int WPE, bool OUT_BF16, bool PRESCALE_Q, bool LOGSIZE>
+// SPLIT: the blocks run key-range pieces of the split last round of work items and store
+// partial softmax states (merge_pieces_kernel finishes them); otherwise one block = one item.
+template <int QB, int WPE, bool OUT_BF16, bool PRESCALE_Q, bool LOGSIZE, bool SPLIT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 void attn_bf16_kernel(AttnArgs a) {
   static_assert(!(LOGSIZE && PRESCALE_Q), "size-aware keys use the exact scale");
+  static_assert(!(SPLIT && (LOGSIZE || PRESCALE_Q)), "split pieces use the plain exact-scale form");
   constexpr bool kExactScale = !PRESCALE_Q;
   constexpr int WQ = 16 * QB;  // query rows per wave
   constexpr int BM = 4 * WQ;   // query rows per work-group
@@ -129,28 +145,34 @@ void attn_bf16_kernel(AttnArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, grp = lane >> 4;
-  const int h = blockIdx.x / a.qtiles, qt = blockIdx.x - h * a.qtiles;
-
-  int64_t row0, row_end, seg;
-  if (a.g2f) {
-    const int f = qt / a.qtiles_per_frame, qf = qt - f * a.qtiles_per_frame;
-    row0 = int64_t(f) * a.g.L + int64_t(qf) * BM;
-    row_end = int64_t(f + 1) * a.g.L;
-    seg = f;
-  } else {
-    row0 = int64_t(qt) * BM;
-    row_end = a.T;
-    seg = 0;
+  // Key tiles [tb, tb + nkt) of the segment: all of them, or one piece of a split item.  (The
+  // whole-item form keeps the bound a kernel argument: a computed bound costs registers.)
+  // A piece sees its tiles as 0 .. nkt-1: the segment pointers move to its first tile and the
+  // tile/key bounds are rebased once (the tile offset itself never enters the loop).
+  int64_t item = blockIdx.x;
+  int piece = 0, tb = 0, nkt = a.nktiles;
+  int slow_from = a.slow_from, nkeys = a.nkeys, n_plain = a.n_plain;
+  if constexpr (SPLIT) {
+    item = a.split_from + blockIdx.x / a.nsplit;
+    piece = int(blockIdx.x % a.nsplit);
+    tb = int(int64_t(piece) * a.nktiles / a.nsplit);
+    nkt = int(int64_t(piece + 1) * a.nktiles / a.nsplit) - tb;
+    slow_from -= tb;
+    nkeys -= tb * kTile;
+    n_plain -= tb * kTile;
   }
+  const ItemRows ir = item_rows(a, item, BM);
+  const int h = ir.h;
+  const int64_t row0 = ir.row0, row_end = ir.row_end, seg = ir.seg;
   const int64_t wrow0 = row0 + int64_t(wave) * WQ;
 
   const uint16_t* Q = static_cast<const uint16_t*>(a.q) + size_t(h) * size_t(a.T) * kHeadDim;
   const uint16_t* Kin = static_cast<const uint16_t*>(a.k) + size_t(h) * size_t(a.T) * kHeadDim;
   const uint16_t* Vin = static_cast<const uint16_t*>(a.v) + size_t(h) * size_t(a.T) * kHeadDim;
-  const size_t seg_off = (size_t(h) * a.rows_per_head + size_t(seg) * a.segment_rows) * kHeadDim;
+  const size_t seg_off = (size_t(h) * a.rows_per_head + size_t(seg) * a.segment_rows + size_t(tb) * kTile) * kHeadDim;
   const uint16_t* kseg = static_cast<const uint16_t*>(a.kpack) + seg_off;
   const uint16_t* vseg = static_cast<const uint16_t*>(a.vpack) + seg_off;
-  const float* bseg = LOGSIZE ? a.kbias + size_t(seg) * a.segment_rows : nullptr;
+  const float* bseg = LOGSIZE ? a.kbias + size_t(seg) * a.segment_rows + size_t(tb) * kTile : nullptr;
 
   // Q as the B operand of S^T = K Q^T: lane (l16, grp) holds query l16 of its block and
   // channels cc*32 + grp*8 .. +7 for cc = 0, 1.
@@ -170,7 +192,8 @@ void attn_bf16_kernel(AttnArgs a) {
     const int64_t t = wrow0 + qb * 16 + l16;
     const bool valid = t < row_end;
     float dot = 0.f;
-    const bool self = a.diag && valid && !token_kept(a.g, t);
+    // The diagonal term belongs to one piece of a split item only.
+    const bool self = a.diag && valid && piece == 0 && !token_kept(a.g, t);
 #pragma unroll
     for (int cc = 0; cc < 2; ++cc) {
       uint4 raw = make_uint4(0, 0, 0, 0), kraw = make_uint4(0, 0, 0, 0);
@@ -271,18 +294,18 @@ void attn_bf16_kernel(AttnArgs a) {
   };
   // Mean-key bias and padding mask, only for the last tiles of the segment.
   auto bias_mask = [&](int j, f32x4_t (&s)[QB][4]) {
-    if (j < a.slow_from) return;
+    if (j < slow_from) return;
 #pragma unroll
     for (int k4 = 0; k4 < 4; ++k4) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int key = j * kTile + k4 * 16 + grp * 4 + i;
         float bias = 0.f;
-        if (key >= a.n_plain) {
-          if constexpr (PRESCALE_Q) bias = mean_bias(a, a.mean_bias_log2, key - a.n_plain);
-          else bias = mean_bias(a, a.mean_bias_s, key - a.n_plain);
+        if (key >= n_plain) {
+          if constexpr (PRESCALE_Q) bias = mean_bias(a, a.mean_bias_log2, key - n_plain);
+          else bias = mean_bias(a, a.mean_bias_s, key - n_plain);
         }
-        const float add = key >= a.nkeys ? -INFINITY : bias;
+        const float add = key >= nkeys ? -INFINITY : bias;
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) s[qb][k4][i] += add;
       }
@@ -360,7 +383,6 @@ void attn_bf16_kernel(AttnArgs a) {
     }
   };
 
-  const int nkt = a.nktiles;
   async_tile(kseg, 0, kbuf0);
   async_bias(0, bbuf0);
   async_tile(vseg, 0, vbuf0);
@@ -438,7 +460,7 @@ void attn_bf16_kernel(AttnArgs a) {
     }
   }
   int j = 0;  // always even at the top of these loops
-  for (; j + 2 < nkt && j + 2 < a.slow_from; j += 2) {
+  for (; j + 2 < nkt && j + 2 < slow_from; j += 2) {
     step(even_t{}, plain_t{}, j, sa, sb);
     step(odd_t{}, plain_t{}, j + 1, sb, sa);
   }
@@ -453,7 +475,22 @@ void attn_bf16_kernel(AttnArgs a) {
     last(even_t{}, sa);
   }
 
-  // ---- epilogue: O / l ----
+  // ---- epilogue: O / l, or the unnormalised state of a piece ----
+  if constexpr (SPLIT) {
+    float* dst = a.part + size_t(blockIdx.x) * BM * kPartRow;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const float l = group_sum(l_run[qb]);
+      float* row = dst + size_t(wave * WQ + qb * 16 + l16) * kPartRow;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) *reinterpret_cast<f32x4_t*>(row + db * 16 + grp * 4) = o[qb][db];
+      if (grp == 0) {
+        row[64] = m_run[qb];
+        row[65] = l;
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const float l = group_sum(l_run[qb]);
@@ -471,6 +508,41 @@ void attn_bf16_kernel(AttnArgs a) {
         *reinterpret_cast<f32x4_t*>(static_cast<float*>(a.out) + off) = r;
       }
     }
+  }
+}
+
+// Merge of the pieces of split work items: for each query row, the pieces' running maxima,
+// sums and unnormalised outputs combine exactly as the online softmax would have across the
+// whole key range.  One thread per (row, 4 channels); rows past the segment end are skipped.
+template <bool OUT_BF16>
+__global__ __launch_bounds__(256) void merge_pieces_kernel(AttnArgs a, int BM, float m_scale) {
+  const int64_t gid = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t rr = gid >> 4;  // row over all split items
+  const int chunk = int(gid & 15);
+  const int64_t k = rr / BM;
+  const int r = int(rr - k * BM);
+  const ItemRows ir = item_rows(a, a.split_from + k, BM);
+  const int64_t t = ir.row0 + r;
+  if (t >= ir.row_end) return;
+  const float* base = a.part + (size_t(k) * a.nsplit * BM + r) * kPartRow;
+  const size_t piece_stride = size_t(BM) * kPartRow;
+  float mx = -INFINITY;
+  for (int p = 0; p < a.nsplit; ++p) mx = fmaxf(mx, base[p * piece_stride + 64]);
+  float l = 0.f;
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  for (int p = 0; p < a.nsplit; ++p) {
+    const float* row = base + p * piece_stride;
+    const float e = __builtin_amdgcn_exp2f((row[64] - mx) * m_scale);
+    l = fmaf(row[65], e, l);
+    acc += *reinterpret_cast<const f32x4_t*>(row + chunk * 4) * e;
+  }
+  const f32x4_t res = acc * (1.f / l);
+  const size_t off = (size_t(ir.h) * size_t(a.T) + size_t(t)) * kHeadDim + chunk * 4;
+  if constexpr (OUT_BF16) {
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.out) + off) =
+        make_uint2(pack_bf16x2(res[0], res[1]), pack_bf16x2(res[2], res[3]));
+  } else {
+    *reinterpret_cast<f32x4_t*>(static_cast<float*>(a.out) + off) = res;
   }
 }
 
@@ -569,8 +641,8 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
 }  // namespace
 
 hipError_t launch_attend(const vggt_attn_plan_s& p, const void* q, const void* k, const void* v,
-                         void* out, const void* ws, hipStream_t stream) {
-  const char* base = static_cast<const char*>(ws);
+                         void* out, void* ws, hipStream_t stream) {
+  char* base = static_cast<char*>(ws);
   AttnArgs a{};
   a.q = q;
   a.k = k;
@@ -640,22 +712,40 @@ hipError_t launch_attend(const vggt_attn_plan_s& p, const void* q, const void* k
   } else {
     a.qtiles = int((p.T + BM - 1) / BM);
   }
-  const unsigned blocks = unsigned(int64_t(a.qtiles) * p.heads);
+  a.split_from = p.split_from;
+  a.nsplit = p.nsplit;
+  a.part = p.nsplit > 1 ? reinterpret_cast<float*>(base + p.layout.off_part) : nullptr;
+  const unsigned blocks = unsigned(p.split_from);
+  const unsigned pblocks = unsigned(p.split_items * p.nsplit);
   const bool ob = p.out_dtype == VGGT_ATTN_BF16;
   const bool pre = p.prescale_q;  // never set together with log_size
   const bool sz = p.log_size;
-#define VGGT_LAUNCH(QB_, WPE_)                                                                       \
-  do {                                                                                              \
-    if (sz && ob) hipLaunchKernelGGL((attn_bf16_kernel<QB_, WPE_, true, false, true>), dim3(blocks), dim3(256), 0, stream, a);  \
-    else if (sz) hipLaunchKernelGGL((attn_bf16_kernel<QB_, WPE_, false, false, true>), dim3(blocks), dim3(256), 0, stream, a); \
-    else if (ob && pre) hipLaunchKernelGGL((attn_bf16_kernel<QB_, WPE_, true, true, false>), dim3(blocks), dim3(256), 0, stream, a); \
-    else if (ob) hipLaunchKernelGGL((attn_bf16_kernel<QB_, WPE_, true, false, false>), dim3(blocks), dim3(256), 0, stream, a);  \
-    else if (pre) hipLaunchKernelGGL((attn_bf16_kernel<QB_, WPE_, false, true, false>), dim3(blocks), dim3(256), 0, stream, a); \
-    else hipLaunchKernelGGL((attn_bf16_kernel<QB_, WPE_, false, false, false>), dim3(blocks), dim3(256), 0, stream, a);        \
+#define VGGT_LAUNCH(QB_, WPE_)                                                                          \
+  do {                                                                                                 \
+    if (blocks > 0) {                                                                                  \
+      if (sz && ob) hipLaunchKernelGGL((attn_bf16_kernel<QB_, WPE_, true, false, true, false>), dim3(blocks), dim3(256), 0, stream, a);   \
+      else if (sz) hipLaunchKernelGGL((attn_bf16_kernel<QB_, WPE_, false, false, true, false>), dim3(blocks), dim3(256), 0, stream, a);  \
+      else if (ob && pre) hipLaunchKernelGGL((attn_bf16_kernel<QB_, WPE_, true, true, false, false>), dim3(blocks), dim3(256), 0, stream, a); \
+      else if (ob) hipLaunchKernelGGL((attn_bf16_kernel<QB_, WPE_, true, false, false, false>), dim3(blocks), dim3(256), 0, stream, a);  \
+      else if (pre) hipLaunchKernelGGL((attn_bf16_kernel<QB_, WPE_, false, true, false, false>), dim3(blocks), dim3(256), 0, stream, a); \
+      else hipLaunchKernelGGL((attn_bf16_kernel<QB_, WPE_, false, false, false, false>), dim3(blocks), dim3(256), 0, stream, a);        \
+    }                                                                                                  \
+    if (pblocks > 0) {                                                                                 \
+      if (ob) hipLaunchKernelGGL((attn_bf16_kernel<QB_, WPE_, true, false, false, true>), dim3(pblocks), dim3(256), 0, stream, a);       \
+      else hipLaunchKernelGGL((attn_bf16_kernel<QB_, WPE_, false, false, false, true>), dim3(pblocks), dim3(256), 0, stream, a);         \
+    }                                                                                                  \
   } while (0)
   if (p.g2f) VGGT_LAUNCH(QBf, WPEf);
   else VGGT_LAUNCH(QBg, WPEg);
 #undef VGGT_LAUNCH
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.nsplit <= 1) return e;
+  // Split pieces run the exact-scale form: running maxima are raw scores.
+  const float m_scale = a.c_log2;
+  const int64_t threads = p.split_items * BM * 16;
+  const unsigned mblocks = unsigned((threads + 255) / 256);
+  if (ob) hipLaunchKernelGGL((merge_pieces_kernel<true>), dim3(mblocks), dim3(256), 0, stream, a, BM, m_scale);
+  else hipLaunchKernelGGL((merge_pieces_kernel<false>), dim3(mblocks), dim3(256), 0, stream, a, BM, m_scale);
   return hipGetLastError();
 }
 

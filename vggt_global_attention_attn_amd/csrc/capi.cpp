@@ -183,7 +183,7 @@ int vggt_attn_pack_sized(const vggt_attn_plan_t* plan, const void* k, const void
 }
 
 int vggt_attn_attend(const vggt_attn_plan_t* plan, const void* q, const void* k, const void* v,
-                     void* out, const void* workspace, size_t workspace_bytes, void* stream) {
+                     void* out, void* workspace, size_t workspace_bytes, void* stream) {
   if (!plan) return set_error(VGGT_ATTN_EINVAL, "plan is NULL");
   int rc = check_tensors(*plan, q, k, v, out, true);
   if (rc) return rc;

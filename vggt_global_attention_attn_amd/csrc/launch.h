@@ -21,6 +21,6 @@ hipError_t launch_size_bias(const vggt_attn_plan_s& p, const float* log_g, void*
 
 // Attention over the packed keys (bf16 inputs: MFMA kernel; fp32 inputs: fp32 kernel).
 hipError_t launch_attend(const vggt_attn_plan_s& p, const void* q, const void* k, const void* v,
-                         void* out, const void* ws, hipStream_t stream);
+                         void* out, void* ws, hipStream_t stream);
 
 }  // namespace vggt

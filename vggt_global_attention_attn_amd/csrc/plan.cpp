@@ -172,6 +172,28 @@ int build_plan(vggt_attn_plan_s* p, int frames, int grid_h, int grid_w, int n_sp
   if (p->rows_per_head > kMaxPackedRows)
     return fail(err, VGGT_ATTN_EINVAL, "packed rows per head %lld exceed %lld", p->rows_per_head, kMaxPackedRows);
 
+  // bf16 work items and the split of a sparse last round (float32 inputs: one item per 64 rows,
+  // never split; nor are the PRESCALE_Q and LOG_SIZE forms).
+  const int qb = g2f ? VGGT_G2F_QB : VGGT_GLOBAL_QB;
+  const int wpe = g2f ? VGGT_G2F_WPE : VGGT_GLOBAL_WPE;
+  p->block_rows = in_dtype == VGGT_ATTN_BF16 ? 64 * qb : 64;
+  const int64_t qtiles = g2f ? ceil_div(L, p->block_rows) * frames : ceil_div(T, p->block_rows);
+  p->work_items = qtiles * heads;
+  p->split_from = p->work_items;
+  p->split_items = 0;
+  p->nsplit = 1;
+  if (in_dtype == VGGT_ATTN_BF16 && !p->prescale_q && !p->log_size) {
+    const int64_t slots = int64_t(kComputeUnits) * wpe;
+    const int64_t tail = p->work_items % slots;
+    const int64_t nkt = p->segment_rows / kTile;
+    const int64_t pieces = std::min<int64_t>({tail > 0 ? slots / tail : 0, nkt / 4, kMaxSplit});
+    if (tail > 0 && 2 * tail <= slots && pieces >= 2) {
+      p->nsplit = int(pieces);
+      p->split_items = tail;
+      p->split_from = p->work_items - tail;
+    }
+  }
+
   p->elem_bytes = in_dtype == VGGT_ATTN_BF16 ? 2 : 4;
   vggt_attn_layout_t& lay = p->layout;
   lay.segments = p->segments;
@@ -185,6 +207,8 @@ int build_plan(vggt_attn_plan_s* p, int frames, int grid_h, int grid_w, int n_sp
   lay.off_partial = off; off = align256(off + int64_t(heads) * partials * 2 * head_dim * 4);
   lay.off_kbias = off;  off = align256(off + (p->log_size ? p->rows_per_head * 4 : 0));
   lay.off_logsize = off; off = align256(off + (p->log_size ? T * 4 : 0));
+  lay.off_part = off;   off = align256(off + p->split_items * p->nsplit * p->block_rows * kPartRow * 4 * (p->nsplit > 1));
+  lay.split_pieces = p->nsplit > 1 ? p->nsplit : 0;
   lay.off_kpack = off;  off = align256(off + int64_t(heads) * p->rows_per_head * head_dim * int64_t(p->elem_bytes));
   lay.off_vpack = off;  off = align256(off + int64_t(heads) * p->rows_per_head * head_dim * int64_t(p->elem_bytes));
   lay.total_bytes = off;

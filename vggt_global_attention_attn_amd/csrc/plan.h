@@ -19,6 +19,29 @@ constexpr int64_t kMaxPackedRows = 16000000;  // per head, keeps row*64 within i
 
 constexpr int kMaxPhases = 9;  // s_h * s_w for the largest window (3 x 3)
 
+// Tiling of the bf16 attention kernel: 16-row query blocks per wave (QB), waves of one work-group
+// per SIMD (WPE).  A work-group has 4 waves and owns 64*QB query rows.
+#ifndef VGGT_GLOBAL_QB
+#define VGGT_GLOBAL_QB 3
+#endif
+#ifndef VGGT_GLOBAL_WPE
+#define VGGT_GLOBAL_WPE 2
+#endif
+#ifndef VGGT_G2F_QB
+#define VGGT_G2F_QB 2
+#endif
+#ifndef VGGT_G2F_WPE
+#define VGGT_G2F_WPE 2
+#endif
+// Work-groups resident at once on a 256-CU gfx950 part (MI355X): one per SIMD set per unit of
+// WPE.  Used only to size the last round of work-groups (see kMaxSplit); correctness does not
+// depend on it.
+constexpr int kComputeUnits = 256;
+// A last round of work-groups that would fill at most half of the resident slots is split
+// along the key range into up to this many pieces, merged afterwards.
+constexpr int kMaxSplit = 8;
+constexpr int kPartRow = 68;  // floats per query row of a piece: O[64], m, l, 2 unused
+
 // Geometry the device code needs to enumerate S and the mean frames and to test membership in
 // closed form.  Compressed frame f has grid phase k = f mod nphase (nphase = s_h*s_w with the
 // phase-shifted grid, else 1), row offset k / s_w and column offset k % s_w; every quantity of
@@ -60,6 +83,10 @@ struct vggt_attn_plan_s {
   double mean_bias_s[vggt::kMaxPhases];  // per phase (per-frame scope) or [0] (single mean):
                                          // COUNT bias in raw-score units, ln(n) / tau
   int64_t segments, segment_rows, keys_per_segment, n_plain, rows_per_head;
+  // bf16 attention work split: work items (query tile x head) below split_from run whole; the
+  // split_items after them run as nsplit key-range pieces each, merged by a second kernel.
+  int64_t work_items, split_from, split_items;
+  int nsplit, block_rows;
   double flops;
   size_t elem_bytes;
   vggt_attn_layout_t layout;
