@@ -177,7 +177,7 @@ void attn_bf16_kernel(AttnArgs a) {
   // Q as the B operand of S^T = K Q^T: lane (l16, grp) holds query l16 of its block and
   // channels cc*32 + grp*8 .. +7 for cc = 0, 1.
   bf16x8_t qf[QB][2];
-  float m_run[QB], l_run[QB];  // running max (log2 units) and lane-partial row sum
+  float m_run[QB], l_run[QB];  // running max (raw scores; log2 units under PRESCALE_Q), lane-partial row sum
   f32x4_t o[QB][4];
   // Two ways to reach log2 units.  Exact (default): Q is used as given, scores and the running
   // max are in units of q.k, and the exp2 argument is multiplied by c = tau*log2(e).
