@@ -40,6 +40,9 @@ constexpr int kComputeUnits = 256;
 // A last round of work-groups that would fill at most half of the resident slots is split
 // along the key range into up to this many pieces, merged afterwards.
 constexpr int kMaxSplit = 8;
+// gfx950 (MI355X) dispatches the work-groups of a launch to its 8 XCDs round-robin; each XCD
+// has its own L2.  Used only to order work items; correctness does not depend on it.
+constexpr int kXcds = 8;
 constexpr int kPartRow = 68;  // floats per query row of a piece: O[64], m, l, 2 unused
 
 // Geometry the device code needs to enumerate S and the mean frames and to test membership in
