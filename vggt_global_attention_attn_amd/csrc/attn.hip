@@ -34,6 +34,9 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 // s_waitcnt immediate for vmcnt(0) with expcnt and lgkmcnt left at their maxima (gfx9 encoding).
 constexpr int kWaitVmcnt0 = 0x0F70;
 constexpr bf16x2_t kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
+// Word 3 of a raw buffer descriptor on gfx9-family parts (gfx950 included): 32-bit data format,
+// no swizzle, so that offsets are plain byte offsets range-checked against num_records.
+constexpr int kBufferWord3 = 0x00020000;
 
 struct AttnArgs {
   const void* q;
@@ -155,7 +158,9 @@ void attn_bf16_kernel(AttnArgs a) {
   auto vbuf = [&](auto par) -> uint8_t* { if constexpr (decltype(par)::value == 0) return vbuf0; else return vbuf1; };
   auto bbuf = [&](auto par) -> float* { if constexpr (decltype(par)::value == 0) return bbuf0; else return bbuf1; };
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // The wave index is uniform: keeping it in a scalar register makes every LDS destination of
+  // the tile copies a scalar (m0) value.
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, grp = lane >> 4;
   // Key tiles [tb, tb + nkt) of the segment: all of them, or one piece of a split item.  (The
   // whole-item form keeps the bound a kernel argument: a computed bound costs registers.)
@@ -254,30 +259,34 @@ void attn_bf16_kernel(AttnArgs a) {
     }
   }
 
-  // Global -> LDS copy of one 64x128-byte tile with global_load_lds_dwordx4: lane L of a wave
+  // Global -> LDS copy of one 64x128-byte tile with buffer_load_dwordx4 ... lds: lane L of a wave
   // instruction writes the 16 bytes at LDS base + 16*L, so each lane fetches the global chunk
   // that belongs at that position of the swizzled layout.  8 wave instructions per tile (2 per
   // wave); no registers are used and completion is awaited (vmcnt) before the step's barrier.
+  // The tile's address lives in a buffer descriptor (scalar registers, advanced per tile); the
+  // lane's byte offset within the tile is the same for every tile, so a copy costs no vector ALU
+  // work.  Instruction i fills KB i*4 + wave of the tile: rows blk*8 + (lane >> 3), whose low
+  // three bits are lane >> 3, so both instructions use the same chunk swizzle.
+  const int tile_off = (wave * 8 + (lane >> 3)) * 128 + (((lane & 7) ^ (lane >> 3)) << 4);
   auto async_tile = [&](const uint16_t* base, int j, uint8_t* buf) {
-    const uint8_t* t = reinterpret_cast<const uint8_t*>(base + size_t(j) * kTile * kHeadDim);
+    const auto rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(base + size_t(j) * kTile * kHeadDim), 0, kTile * 128, kBufferWord3);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int blk = i * 4 + wave;              // which 1 KB of the tile this instruction fills
-      const int row = blk * 8 + (lane >> 3);     // 8 rows of 128 bytes per KB
-      const int ch = (lane & 7) ^ (row & 7);     // global chunk that lands at position lane & 7
-      __builtin_amdgcn_global_load_lds(
-          (__attribute__((address_space(1))) void*)(t + row * 128 + ch * 16),
-          (__attribute__((address_space(3))) void*)(buf + blk * 1024), 16, 0, 0);
-    }
+    for (int i = 0; i < 2; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rsrc, (__attribute__((address_space(3))) void*)(buf + (i * 4 + wave) * 1024), 16,
+          tile_off + i * 4096, 0, 0, 0);
   };
-  // Key biases of tile j: wave 0 copies the 64 floats with 4-byte global->LDS loads (lane L
-  // lands at LDS base + 4*L).
+  // Key biases of tile j: wave 0 copies the 64 floats with 4-byte loads (lane L lands at LDS
+  // base + 4*L).
   auto async_bias = [&](int j, float* buf) {
     if constexpr (LOGSIZE) {
-      if (wave == 0)
-        __builtin_amdgcn_global_load_lds(
-            (__attribute__((address_space(1))) void*)(bseg + size_t(j) * kTile + lane),
-            (__attribute__((address_space(3))) void*)buf, 4, 0, 0);
+      if (wave == 0) {
+        const auto rsrc = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<float*>(bseg + size_t(j) * kTile), 0, kTile * 4, kBufferWord3);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)buf, 4,
+                                                 lane * 4, 0, 0, 0);
+      }
     }
   };
   auto wait_tiles = [&]() { __builtin_amdgcn_s_waitcnt(kWaitVmcnt0); };
