@@ -117,7 +117,9 @@ typedef struct {
   int64_t split_pieces;      /* key-range pieces per work item of that round (0 = no split)   */
   int64_t off_kpack;         /* [H][segments*segment_rows][d] input dtype                    */
   int64_t off_vpack;         /* bf16: [H][rows/64][d][64] key-minor tiles (see below);
-                                fp32: [H][rows][d]                                           */
+                                fp32: [H][rows][d].  Both parts are empty (off_kpack ==
+                                off_vpack == total_bytes) for bf16 G2F plans, whose attention
+                                stage reads k and v directly (a frame's keys are its tokens) */
   int64_t total_bytes;
 } vggt_attn_layout_t;
 
@@ -169,13 +171,16 @@ int vggt_attn_forward(const vggt_attn_plan_t* plan, const void* q, const void* k
  * stand for, rounded to the input dtype: per frame over its dropped patches, or once over all
  * dropped patches with MEAN_GLOBAL, or once over all T tokens with G2M) and their logit
  * biases, and the packed keys and values: rows [0,|S|) are exact copies of K/V rows of S, rows
- * [|S|, |S|+M) the means, padding rows zero.  Under G2F (and sigma = 1) it packs every token,
- * frame by frame.  |D_f| is L for every frame under G2M.  Reads k and v only. */
+ * [|S|, |S|+M) the means, padding rows zero.  Under sigma = 1 it packs every token; under G2F
+ * float32 plans pack every token frame by frame, while bf16 plans write |D_f| only, since their
+ * attention stage reads k and v in place.  |D_f| is L for every frame under G2M.  Reads k and
+ * v only. */
 int vggt_attn_pack(const vggt_attn_plan_t* plan, const void* k, const void* v, void* workspace,
                    size_t workspace_bytes, void* stream);
 
 /* Attention stage on a workspace already filled by vggt_attn_pack for the same plan and the
- * same k, v (k and v are read again for the diagonal term).  Writes every element of out.  It
+ * same k, v (k and v are read again for the diagonal term, and for every key by bf16 G2F
+ * plans, which keep no packed copy).  Writes every element of out.  It
  * uses the workspace's off_part area as scratch (the partial softmax states of a split last
  * round of work-groups, see vggt_attn_layout_t) and leaves the packed parts unchanged, so it
  * may be called again on the same workspace. */

@@ -91,6 +91,16 @@ def test_plan_counts_match_oracle(va, desc):
         assert lay["off_logsize"] - lay["off_kbias"] >= 4 * lay["segments"] * lay["segment_rows"]
         assert lay["off_kpack"] - lay["off_logsize"] >= 4 * desc.T
     assert lay["total_bytes"] == p.workspace_bytes
+    # The packed parts hold H x padded rows x d values, except for bf16 G2F plans, whose keys
+    # (each frame's own tokens) are read in place.
+    inplace = desc.g2f
+    rows = lay["segments"] * lay["segment_rows"]
+    kbytes = lay["off_vpack"] - lay["off_kpack"]
+    if inplace:
+        assert kbytes == 0 and lay["total_bytes"] == lay["off_vpack"]
+    else:
+        assert kbytes >= desc.heads * rows * desc.head_dim * 2
+        assert lay["total_bytes"] - lay["off_vpack"] >= desc.heads * rows * desc.head_dim * 2
 
 
 def test_config5_sizes(va):

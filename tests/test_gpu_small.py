@@ -115,7 +115,8 @@ def key_at(p):
     return half * 32 + (g * 4 + j if j < 4 else 16 + g * 4 + (j - 4))
 
 
-PACKED = [CASES[3], CASES[5], CASES[6], CASES[7], NEW["sga6-phase-count"], NEW["sga4-global-count-phase"],
+# Plans with a packed copy (bf16 G2F plans read K/V in place and have none).
+PACKED = [CASES[3], CASES[5], CASES[7], NEW["sga6-phase-count"], NEW["sga4-global-count-phase"],
           NEW["sga2-phase-empty-sets"], NEW["g2m"]]
 
 
@@ -137,14 +138,6 @@ def test_packed_rows(lib, desc, label):
     vrows = np.zeros((H, rows // 64, 64, d), dtype=np.uint16)
     vrows[:, :, perm, :] = vt.transpose(0, 1, 3, 2)
     vrows = vrows.reshape(H, rows, d)
-    if desc.g2f:
-        for f in range(desc.frames):
-            seg = slice(f * lay["segment_rows"], f * lay["segment_rows"] + desc.L)
-            tok = slice(f * desc.L, (f + 1) * desc.L)
-            assert np.array_equal(kp[:, seg], k[:, tok]) and np.array_equal(vrows[:, seg], v[:, tok])
-            pad = slice(f * lay["segment_rows"] + desc.L, (f + 1) * lay["segment_rows"])
-            assert not kp[:, pad].any() and not vrows[:, pad].any()
-        return
     S = oracle.index_set(desc)
     nS = S.size
     assert np.array_equal(kp[:, :nS], k[:, S]) and np.array_equal(vrows[:, :nS], v[:, S])

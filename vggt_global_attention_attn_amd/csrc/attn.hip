@@ -31,6 +31,8 @@ namespace vggt {
 namespace {
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x8_t __attribute__((ext_vector_type(8)));
 // s_waitcnt immediate for vmcnt(0) with expcnt and lgkmcnt left at their maxima (gfx9 encoding).
 constexpr int kWaitVmcnt0 = 0x0F70;
 constexpr bf16x2_t kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
@@ -133,7 +135,9 @@ __device__ __forceinline__ float group_sum(float x) {
 
 // SPLIT: the blocks run key-range pieces of the split last round of work items and store
 // partial softmax states (merge_pieces_kernel finishes them); otherwise one block = one item.
-template <int QB, int WPE, bool OUT_BF16, bool PRESCALE_Q, bool LOGSIZE, bool SPLIT>
+// INPLACE (G2F): the keys of a frame are its tokens, so K and V tiles are copied from the input
+// tensors instead of the packed workspace, and V is read transposed out of LDS.
+template <int QB, int WPE, bool OUT_BF16, bool PRESCALE_Q, bool LOGSIZE, bool SPLIT, bool INPLACE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 void attn_bf16_kernel(AttnArgs a) {
   static_assert(!(LOGSIZE && PRESCALE_Q), "size-aware keys use the exact scale");
@@ -186,9 +190,23 @@ void attn_bf16_kernel(AttnArgs a) {
   const uint16_t* Q = static_cast<const uint16_t*>(a.q) + size_t(h) * size_t(a.T) * kHeadDim;
   const uint16_t* Kin = static_cast<const uint16_t*>(a.k) + size_t(h) * size_t(a.T) * kHeadDim;
   const uint16_t* Vin = static_cast<const uint16_t*>(a.v) + size_t(h) * size_t(a.T) * kHeadDim;
-  const size_t seg_off = (size_t(h) * a.rows_per_head + size_t(seg) * a.segment_rows + size_t(tb) * kTile) * kHeadDim;
-  const uint16_t* kseg = static_cast<const uint16_t*>(a.kpack) + seg_off;
-  const uint16_t* vseg = static_cast<const uint16_t*>(a.vpack) + seg_off;
+  // Key rows of this item from kseg/vseg on: the packed segment, or (INPLACE) the tokens from
+  // the first key of the item's range, of which kv_rows remain in the head's tensor (a tile
+  // that runs past them is cut by its copy's range check, which lands zeros; they are masked).
+  const uint16_t* kseg;
+  const uint16_t* vseg;
+  int64_t kv_rows;
+  if constexpr (INPLACE) {
+    const int64_t first = (a.g2f ? seg * a.g.L : 0) + int64_t(tb) * kTile;
+    kseg = Kin + size_t(first) * kHeadDim;
+    vseg = Vin + size_t(first) * kHeadDim;
+    kv_rows = a.T - first;
+  } else {
+    const size_t seg_off = (size_t(h) * a.rows_per_head + size_t(seg) * a.segment_rows + size_t(tb) * kTile) * kHeadDim;
+    kseg = static_cast<const uint16_t*>(a.kpack) + seg_off;
+    vseg = static_cast<const uint16_t*>(a.vpack) + seg_off;
+    kv_rows = int64_t(a.nktiles) * kTile;
+  }
   const float* bseg = LOGSIZE ? a.kbias + size_t(seg) * a.segment_rows + size_t(tb) * kTile : nullptr;
 
   // Q as the B operand of S^T = K Q^T: lane (l16, grp) holds query l16 of its block and
@@ -266,16 +284,21 @@ void attn_bf16_kernel(AttnArgs a) {
   // The tile's address lives in a buffer descriptor (scalar registers, advanced per tile); the
   // lane's byte offset within the tile is the same for every tile, so a copy costs no vector ALU
   // work.  Instruction i fills KB i*4 + wave of the tile: rows blk*8 + (lane >> 3), whose low
-  // three bits are lane >> 3, so both instructions use the same chunk swizzle.
-  const int tile_off = (wave * 8 + (lane >> 3)) * 128 + (((lane & 7) ^ (lane >> 3)) << 4);
-  auto async_tile = [&](const uint16_t* base, int j, uint8_t* buf) {
+  // three bits are lane >> 3, so both instructions use the same chunk swizzle.  K tiles (and
+  // packed V tiles) swizzle 16-byte chunks by row & 7; row-major V tiles of the INPLACE form by
+  // row & 6, which spreads their transposed reads over the banks.
+  const int k_off = (wave * 8 + (lane >> 3)) * 128 + (((lane & 7) ^ (lane >> 3)) << 4);
+  const int v_off = INPLACE ? (wave * 8 + (lane >> 3)) * 128 + (((lane & 7) ^ ((lane >> 3) & 6)) << 4) : k_off;
+  auto async_tile = [&](const uint16_t* base, int j, uint8_t* buf, int v_tile) {
+    const int lane_off = INPLACE && v_tile ? v_off : k_off;
+    const int rows = INPLACE ? int(min(kv_rows - int64_t(j) * kTile, int64_t(kTile))) : kTile;
     const auto rsrc = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(base + size_t(j) * kTile * kHeadDim), 0, kTile * 128, kBufferWord3);
+        const_cast<uint16_t*>(base + size_t(j) * kTile * kHeadDim), 0, rows * 128, kBufferWord3);
 #pragma unroll
     for (int i = 0; i < 2; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           rsrc, (__attribute__((address_space(3))) void*)(buf + (i * 4 + wave) * 1024), 16,
-          tile_off + i * 4096, 0, 0, 0);
+          lane_off + i * 4096, 0, 0, 0);
   };
   // Key biases of tile j: wave 0 copies the 64 floats with 4-byte loads (lane L lands at LDS
   // base + 4*L).
@@ -295,12 +318,41 @@ void attn_bf16_kernel(AttnArgs a) {
     return *reinterpret_cast<const bf16x8_t*>(&buf[row * 128 + ((ch ^ (row & 7)) << 4)]);
   };
 
-  // K (or V) operand fragments of a tile: read once per step, shared by every query block.
+  // K (or packed V) operand fragments of a tile: read once per step, shared by every query block.
   auto k_frags = [&](const uint8_t* kb, bf16x8_t (&kf)[4][2]) {
 #pragma unroll
     for (int k4 = 0; k4 < 4; ++k4) {
       kf[k4][0] = lds_frag(kb, k4 * 16 + l16, grp);
       kf[k4][1] = lds_frag(kb, k4 * 16 + l16, 4 + grp);
+    }
+  };
+  // V^T operand fragments from a row-major V tile (INPLACE) with ds_read_b64_tr_b16.  Within
+  // each 16-lane group, lane j of the instruction reads 4 consecutive values of its own address
+  // (row j of a 16 x 4 block) and lane i receives column i & 3 of rows 4r + (i >> 2), r = 0..3.
+  // Lane j = (l16 of this lane) therefore addresses key 4*grp + (j >> 2) (+ 16u + 32h) and the
+  // channels db*16 + 4*(j & 3) .. +3, so that lane i ends up with channel db*16 + i of keys
+  // 4*grp + r, the order in which P leaves the score blocks; u = 1 gives the keys 16 further on.
+  const int vt_row = 4 * grp + (l16 >> 2);
+  int vt_addr[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+    vt_addr[db] = vt_row * 128 + (((2 * db + ((l16 >> 1) & 1)) ^ (vt_row & 6)) << 4) + 8 * (l16 & 1);
+  auto v_frags = [&](const uint8_t* vb, bf16x8_t (&vf)[4][2]) {
+    if constexpr (!INPLACE) {
+      k_frags(vb, vf);
+    } else {
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const uint8_t* p0 = vb + vt_addr[db] + hh * 4096;
+          const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) i16x4_t*)(p0));
+          const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) i16x4_t*)(p0 + 2048));
+          vf[db][hh] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+      }
     }
   };
   // S^T = K Q^T for 64 keys x the 16 queries of block qb: s[k4][i] is key k4*16 + grp*4 + i.
@@ -411,11 +463,11 @@ void attn_bf16_kernel(AttnArgs a) {
     }
   };
 
-  async_tile(kseg, 0, kbuf0);
+  async_tile(kseg, 0, kbuf0, 0);
   async_bias(0, bbuf0);
-  async_tile(vseg, 0, vbuf0);
+  async_tile(vseg, 0, vbuf0, 1);
   if (nkt > 1) {
-    async_tile(kseg, 1, kbuf1);
+    async_tile(kseg, 1, kbuf1, 0);
     async_bias(1, bbuf1);
   }
   wait_tiles();
@@ -430,12 +482,12 @@ void attn_bf16_kernel(AttnArgs a) {
     constexpr int P = decltype(parity)::value;
     using same_t = std::integral_constant<int, P>;
     using other_t = std::integral_constant<int, P ^ 1>;
-    async_tile(kseg, min(j + 2, nkt - 1), kbuf(same_t{}));
+    async_tile(kseg, min(j + 2, nkt - 1), kbuf(same_t{}), 0);
     async_bias(min(j + 2, nkt - 1), bbuf(same_t{}));
-    async_tile(vseg, j + 1, vbuf(other_t{}));
+    async_tile(vseg, j + 1, vbuf(other_t{}), 1);
     bf16x8_t kf[4][2], vf[4][2];
     k_frags(kbuf(other_t{}), kf);
-    k_frags(vbuf(same_t{}), vf);
+    v_frags(vbuf(same_t{}), vf);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       bf16x8_t pf[2];
@@ -448,7 +500,7 @@ void attn_bf16_kernel(AttnArgs a) {
   };
   auto last = [&](auto parity, f32x4_t (&s_cur)[QB][4]) {
     bf16x8_t kf[4][2], vf[4][2];
-    k_frags(vbuf(parity), vf);
+    v_frags(vbuf(parity), vf);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       bf16x8_t pf[2];
@@ -755,23 +807,24 @@ hipError_t launch_attend(const vggt_attn_plan_s& p, const void* q, const void* k
   const bool ob = p.out_dtype == VGGT_ATTN_BF16;
   const bool pre = p.prescale_q;  // never set together with log_size
   const bool sz = p.log_size;
-#define VGGT_LAUNCH(QB_, WPE_)                                                                          \
+#define VGGT_LAUNCH(QB_, WPE_, IP_)                                                                     \
   do {                                                                                                 \
     if (blocks > 0) {                                                                                  \
-      if (sz && ob) hipLaunchKernelGGL((attn_bf16_kernel<QB_, WPE_, true, false, true, false>), dim3(blocks), dim3(256), 0, stream, a);   \
-      else if (sz) hipLaunchKernelGGL((attn_bf16_kernel<QB_, WPE_, false, false, true, false>), dim3(blocks), dim3(256), 0, stream, a);  \
-      else if (ob && pre) hipLaunchKernelGGL((attn_bf16_kernel<QB_, WPE_, true, true, false, false>), dim3(blocks), dim3(256), 0, stream, a); \
-      else if (ob) hipLaunchKernelGGL((attn_bf16_kernel<QB_, WPE_, true, false, false, false>), dim3(blocks), dim3(256), 0, stream, a);  \
-      else if (pre) hipLaunchKernelGGL((attn_bf16_kernel<QB_, WPE_, false, true, false, false>), dim3(blocks), dim3(256), 0, stream, a); \
-      else hipLaunchKernelGGL((attn_bf16_kernel<QB_, WPE_, false, false, false, false>), dim3(blocks), dim3(256), 0, stream, a);        \
+      if (sz && ob) hipLaunchKernelGGL((attn_bf16_kernel<QB_, WPE_, true, false, true, false, IP_>), dim3(blocks), dim3(256), 0, stream, a);   \
+      else if (sz) hipLaunchKernelGGL((attn_bf16_kernel<QB_, WPE_, false, false, true, false, IP_>), dim3(blocks), dim3(256), 0, stream, a);  \
+      else if (ob && pre) hipLaunchKernelGGL((attn_bf16_kernel<QB_, WPE_, true, true, false, false, IP_>), dim3(blocks), dim3(256), 0, stream, a); \
+      else if (ob) hipLaunchKernelGGL((attn_bf16_kernel<QB_, WPE_, true, false, false, false, IP_>), dim3(blocks), dim3(256), 0, stream, a);  \
+      else if (pre) hipLaunchKernelGGL((attn_bf16_kernel<QB_, WPE_, false, true, false, false, IP_>), dim3(blocks), dim3(256), 0, stream, a); \
+      else hipLaunchKernelGGL((attn_bf16_kernel<QB_, WPE_, false, false, false, false, IP_>), dim3(blocks), dim3(256), 0, stream, a);        \
     }                                                                                                  \
     if (pblocks > 0) {                                                                                 \
-      if (ob) hipLaunchKernelGGL((attn_bf16_kernel<QB_, WPE_, true, false, false, true>), dim3(pblocks), dim3(256), 0, stream, a);       \
-      else hipLaunchKernelGGL((attn_bf16_kernel<QB_, WPE_, false, false, false, true>), dim3(pblocks), dim3(256), 0, stream, a);         \
+      if (ob) hipLaunchKernelGGL((attn_bf16_kernel<QB_, WPE_, true, false, false, true, IP_>), dim3(pblocks), dim3(256), 0, stream, a);       \
+      else hipLaunchKernelGGL((attn_bf16_kernel<QB_, WPE_, false, false, false, true, IP_>), dim3(pblocks), dim3(256), 0, stream, a);         \
     }                                                                                                  \
   } while (0)
-  if (p.g2f) VGGT_LAUNCH(QBf, WPEf);
-  else VGGT_LAUNCH(QBg, WPEg);
+  // Every bf16 G2F plan reads K/V in place; the global forms read the packed copy.
+  if (p.g2f) VGGT_LAUNCH(QBf, WPEf, true);
+  else VGGT_LAUNCH(QBg, WPEg, false);
 #undef VGGT_LAUNCH
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.nsplit <= 1) return e;

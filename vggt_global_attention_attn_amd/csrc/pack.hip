@@ -225,6 +225,16 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a) {
   }
 }
 
+// Index set and per-frame dropped counts alone, for plans whose attention reads K and V in
+// place (dense and G2F: nothing to gather).
+__global__ __launch_bounds__(256) void index_kernel(PackArgs a) {
+  const int64_t stride = int64_t(gridDim.x) * 256;
+  const int64_t first = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (a.index)
+    for (int64_t i = first; i < a.nS; i += stride) a.index[i] = int32_t(token_of_kept_index(a.g, i));
+  for (int64_t f = first; f < a.frames; f += stride) a.dcount[f] = frame_dropped(a.g, int(f));
+}
+
 struct SizeBiasArgs {
   PackArgs pk;           // geometry of the packed rows (packed_source)
   const float* log_g;    // [T]
@@ -318,6 +328,12 @@ hipError_t launch_pack(const vggt_attn_plan_s& p, const void* k, const void* v, 
   a.segment_rows = int(p.segment_rows);
   a.frames = p.frames;
   a.g = p.geom;
+  if (p.inplace) {
+    const int64_t work = std::max<int64_t>(a.index ? p.nS : 0, p.frames);
+    const unsigned blocks = unsigned(std::min<int64_t>((work + 255) / 256, 4096));
+    hipLaunchKernelGGL(index_kernel, dim3(blocks), dim3(256), 0, stream, a);
+    return hipGetLastError();
+  }
   const dim3 grid(unsigned(p.rows_per_head / kTile), unsigned(p.heads));
   if (p.in_dtype == VGGT_ATTN_BF16)
     hipLaunchKernelGGL((pack_kernel<uint16_t, true>), grid, dim3(256), 0, stream, a);

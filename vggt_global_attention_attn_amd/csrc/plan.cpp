@@ -194,6 +194,7 @@ int build_plan(vggt_attn_plan_s* p, int frames, int grid_h, int grid_w, int n_sp
     }
   }
 
+  p->inplace = in_dtype == VGGT_ATTN_BF16 && g2f;
   p->elem_bytes = in_dtype == VGGT_ATTN_BF16 ? 2 : 4;
   vggt_attn_layout_t& lay = p->layout;
   lay.segments = p->segments;
@@ -209,8 +210,9 @@ int build_plan(vggt_attn_plan_s* p, int frames, int grid_h, int grid_w, int n_sp
   lay.off_logsize = off; off = align256(off + (p->log_size ? T * 4 : 0));
   lay.off_part = off;   off = align256(off + p->split_items * p->nsplit * p->block_rows * kPartRow * 4 * (p->nsplit > 1));
   lay.split_pieces = p->nsplit > 1 ? p->nsplit : 0;
-  lay.off_kpack = off;  off = align256(off + int64_t(heads) * p->rows_per_head * head_dim * int64_t(p->elem_bytes));
-  lay.off_vpack = off;  off = align256(off + int64_t(heads) * p->rows_per_head * head_dim * int64_t(p->elem_bytes));
+  const int64_t packed = p->inplace ? 0 : int64_t(heads) * p->rows_per_head * head_dim * int64_t(p->elem_bytes);
+  lay.off_kpack = off;  off = align256(off + packed);
+  lay.off_vpack = off;  off = align256(off + packed);
   lay.total_bytes = off;
   return VGGT_ATTN_OK;
 }

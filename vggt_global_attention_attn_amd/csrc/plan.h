@@ -86,6 +86,10 @@ struct vggt_attn_plan_s {
   double mean_bias_s[vggt::kMaxPhases];  // per phase (per-frame scope) or [0] (single mean):
                                          // COUNT bias in raw-score units, ln(n) / tau
   int64_t segments, segment_rows, keys_per_segment, n_plain, rows_per_head;
+  // bf16 G2F plans read K and V where they lie (the keys of a frame are its tokens, in order):
+  // no packed copy; the pack stage writes only the per-frame counts.  (Dense plans could do the
+  // same, but there the transposed V reads cost more attention time than the O(T) pack.)
+  bool inplace;
   // bf16 attention work split: work items (query tile x head) below split_from run whole; the
   // split_items after them run as nsplit key-range pieces each, merged by a second kernel.
   int64_t work_items, split_from, split_items;
