@@ -73,11 +73,13 @@ def _rng(seed: int, *key: int) -> np.random.Generator:
 
 def make_qkv(frames: int, grid_h: int, grid_w: int, n_special: int, heads: int, head_dim: int,
              dtype: str = "bf16", seed: int = 0, workers: int | None = None,
-             shared: float = 0.7, noise: float = 0.7):
+             shared: float = 0.7, noise: float = 0.7, tie_qk: bool = False):
     """Draw Q, K, V of shape [heads][frames*L][head_dim].
 
     dtype "bf16" returns uint16 arrays of bfloat16 bits; "fp32" returns float32 arrays.
-    The same (geometry, seed) always gives the same bytes, whatever the worker count."""
+    The same (geometry, seed) always gives the same bytes, whatever the worker count.
+    tie_qk: K takes Q's per-position component (a stress input: a query's logits then peak at
+    its own slot in every frame)."""
     if dtype not in ("bf16", "fp32"):
         raise ValueError(f"dtype must be 'bf16' or 'fp32', got {dtype!r}")
     L = tokens_per_frame(grid_h, grid_w, n_special)
@@ -87,7 +89,8 @@ def make_qkv(frames: int, grid_h: int, grid_w: int, n_special: int, heads: int, 
     result = {}
     with ThreadPoolExecutor(max_workers=workers) as pool:
         for ti, name in enumerate(("q", "k", "v")):
-            u = _rng(seed, ti, 0).standard_normal((heads, L, head_dim), dtype=np.float32)
+            u = _rng(seed, 0 if (tie_qk and name == "k") else ti, 0).standard_normal(
+                (heads, L, head_dim), dtype=np.float32)
             u *= np.float32(shared)
             x = np.empty((heads, T, head_dim), dtype=out_dtype)
 

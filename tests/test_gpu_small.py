@@ -2,7 +2,9 @@
 tails, every form (dense, SGA sigma 2/4/6/9, enhanced SGA with UNIT and COUNT means, pi^3
 without a dense frame, the phase-shifted grid, the global mean scope, G2F, G2M), both output
 types, plus the bit-exact index set and packed rows, V = 1, determinism, a NaN-poisoned
-workspace and the C ABI's error codes.  Every call goes through the C ABI of libvggt_attn.so."""
+workspace, the tied-Q/K stress input, the collapse identity (identical dropped rows under COUNT
+means equal dense attention), G2F's in-place reads stopping at the tensors' end, and the C ABI's
+error codes.  Every call goes through the C ABI of libvggt_attn.so."""
 import ctypes
 import zlib
 
@@ -11,6 +13,7 @@ import pytest
 
 import oracle
 from oracle import Desc
+from synth import make_qkv
 from tests.gpu_util import assert_close, errors, inputs_for, plan_kwargs, to_device
 
 pytestmark = pytest.mark.gpu
@@ -321,3 +324,65 @@ def test_log_size_zero_sizes_equal_plain_path(lib):
     got = run_sized(lib, desc, q, k, v, np.zeros(desc.T, dtype=np.float32))
     _, ref, _, _ = run(lib, plain, q, k, v)
     assert np.array_equal(got, ref)
+
+
+TIED = [(Desc(6, 13, 11, 2, sigma=6, diag=True, mean=True), "sga6-enh"),
+        (Desc(7, 37, 37, 2, sigma=4, diag=True, mean=True, mean_count=True), "sga4-enh-count-37x37"),
+        (Desc(4, 37, 37, 2, g2f=True), "g2f-37x37"),
+        (Desc(3, 37, 37, 2, sigma=1), "dense-37x37")]
+
+
+@pytest.mark.parametrize("desc,label", TIED, ids=[c[1] for c in TIED])
+def test_parity_tied_qk(lib, desc, label):
+    """Stress input: K carries Q's per-position component, so a query's logits peak at its own
+    patch position in every frame (about tau * 0.49 * 64 = 3.9 above the rest), far from the
+    first tile's keys, which moves the running max."""
+    print(f"[tied] {label}", flush=True)
+    q, k, v = make_qkv(desc.frames, desc.grid_h, desc.grid_w, desc.n_special, desc.heads, desc.head_dim,
+                       dtype="bf16", seed=21, tie_qk=True)
+    _, got, _, _ = run(lib, desc, q, k, v)
+    ref = oracle.attention(q, k, v, desc, workers=4)
+    print(label, "tied max-abs %.3e rel-L2 %.3e" % errors(got, ref))
+    assert_close(got, ref, fp32=False, label=label + "/tied")
+
+
+def test_collapse_identity(lib):
+    """Collapse identity: when every dropped K/V row of a frame is the same row, SGA with COUNT
+    means and no diagonal term equals dense attention (a mean key with bias ln|D_f| stands for
+    |D_f| copies of that key).  GPU SGA against the oracle's dense attention."""
+    desc = Desc(5, 13, 11, 2, sigma=6, mean=True, mean_count=True)
+    dense = Desc(5, 13, 11, 2, sigma=1)
+    q, k, v = inputs_for(desc, "bf16", seed=22)
+    kept = set(oracle.index_set(desc).tolist())
+    for f in range(desc.frames):
+        dropped = [t for t in range(f * desc.L, (f + 1) * desc.L) if t not in kept]
+        if dropped:
+            k[:, dropped] = k[:, dropped[:1]]
+            v[:, dropped] = v[:, dropped[:1]]
+    _, got, _, _ = run(lib, desc, q, k, v)
+    ref = oracle.attention(q, k, v, dense, workers=4)
+    assert_close(got, ref, fp32=False, label="collapse")
+
+
+def test_g2f_reads_stop_at_tensor_end(lib):
+    """bf16 G2F reads K and V in place; the last frame's last key tile runs past the end of the
+    tensors and must be cut there by the copies' range check: NaN right after both tensors
+    leaves the output finite and equal to the oracle's."""
+    import torch
+    desc = Desc(3, 13, 11, 2, g2f=True)  # L = 145: the last tile of a frame holds 17 keys
+    q, k, v = inputs_for(desc, "bf16", seed=23)
+    plan = lib.Plan(**plan_kwargs(desc))
+
+    def poisoned(x):
+        n = x.size
+        big = torch.full((n + 64 * 64 * 4,), float("nan"), dtype=torch.bfloat16, device="cuda")
+        big[:n] = to_device(x).reshape(-1)
+        return big[:n].view(x.shape)
+
+    kd, vd = poisoned(k), poisoned(v)
+    out = plan.new_output()
+    ws = plan.new_workspace()
+    plan.forward(to_device(q), kd, vd, out, ws)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy()
+    assert_close(got, oracle.attention(q, k, v, desc), fp32=False, label="g2f-poisoned-tail")
