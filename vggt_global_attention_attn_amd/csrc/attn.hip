@@ -229,53 +229,17 @@ void attn_bf16_kernel(AttnArgs a) {
   // almost never raised.
   const float shift = kExactScale ? a.weight_shift : 0.f;
   const float shift_scale = kExactScale ? a.weight_scale : 1.f;  // 2^-w
+  // Raw Q fragments of every query block, as straight-line range-checked buffer loads (rows
+  // past the head's T read as zero; rows past the item's end are computed but never stored), so
+  // that they are in flight together with the first tile copies issued below.
+  const auto qrsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(Q), 0, int(a.T * 128), kBufferWord3);
+  uint4 qraw[QB][2];
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int64_t t = wrow0 + qb * 16 + l16;
-    const bool valid = t < row_end;
-    float dot = 0.f;
-    // The diagonal term belongs to one piece of a split item only.
-    const bool self = a.diag && valid && piece == 0 && !token_kept(a.g, t);
+  for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-    for (int cc = 0; cc < 2; ++cc) {
-      uint4 raw = make_uint4(0, 0, 0, 0), kraw = make_uint4(0, 0, 0, 0);
-      if (valid) raw = *reinterpret_cast<const uint4*>(Q + size_t(t) * kHeadDim + cc * 32 + grp * 8);
-      if (self) kraw = *reinterpret_cast<const uint4*>(Kin + size_t(t) * kHeadDim + cc * 32 + grp * 8);
-      const uint32_t qw[4] = {raw.x, raw.y, raw.z, raw.w};
-      const uint32_t kw[4] = {kraw.x, kraw.y, kraw.z, kraw.w};
-      bf16x8_t v;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float q0 = __uint_as_float(qw[i] << 16) * qscale, q1 = __uint_as_float(qw[i] & 0xffff0000u) * qscale;
-        v[2 * i] = (__bf16)q0;
-        v[2 * i + 1] = (__bf16)q1;
-        // Diagonal self logit from the same scaled query the matrix core uses.
-        dot = fmaf(float(v[2 * i]), __uint_as_float(kw[i] << 16), dot);
-        dot = fmaf(float(v[2 * i + 1]), __uint_as_float(kw[i] & 0xffff0000u), dot);
-      }
-      qf[qb][cc] = v;
-    }
-    // Diagonal term: a query whose own token is not in S starts with its self term
-    // (m = self logit, weight 2^-w in l and O); the others start empty.
-    dot = group_sum(dot);
-    if constexpr (LOGSIZE) {
-      if (self) dot += a.logsize[t] * a.size_scale;
-    }
-    m_run[qb] = self ? dot : -INFINITY;
-    l_run[qb] = (self && grp == 0) ? shift_scale : 0.f;
-#pragma unroll
-    for (int db = 0; db < 4; ++db) {
-      f32x4_t init = {0.f, 0.f, 0.f, 0.f};
-      if (self) {
-        const uint2 vr = *reinterpret_cast<const uint2*>(Vin + size_t(t) * kHeadDim + db * 16 + grp * 4);
-        init[0] = __uint_as_float(vr.x << 16) * shift_scale;
-        init[1] = __uint_as_float(vr.x & 0xffff0000u) * shift_scale;
-        init[2] = __uint_as_float(vr.y << 16) * shift_scale;
-        init[3] = __uint_as_float(vr.y & 0xffff0000u) * shift_scale;
-      }
-      o[qb][db] = init;
-    }
-  }
+    for (int cc = 0; cc < 2; ++cc)
+      qraw[qb][cc] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+          qrsrc, int(wrow0 + qb * 16 + l16) * 128 + cc * 64 + grp * 16, 0, 0));
 
   // Global -> LDS copy of one 64x128-byte tile with buffer_load_dwordx4 ... lds: lane L of a wave
   // instruction writes the 16 bytes at LDS base + 16*L, so each lane fetches the global chunk
@@ -381,7 +345,7 @@ void attn_bf16_kernel(AttnArgs a) {
       for (int i = 0; i < 4; ++i) {
         const int key = j * kTile + k4 * 16 + grp * 4 + i;
         float bias = 0.f;
-        if (key >= n_plain) {
+        if (!INPLACE && key >= n_plain) {  // (a G2F segment has no mean keys)
           if constexpr (PRESCALE_Q) bias = mean_bias(a, a.mean_bias_log2, key - n_plain);
           else bias = mean_bias(a, a.mean_bias_s, key - n_plain);
         }
@@ -466,12 +430,66 @@ void attn_bf16_kernel(AttnArgs a) {
   async_tile(kseg, 0, kbuf0, 0);
   async_bias(0, bbuf0);
   async_tile(vseg, 0, vbuf0, 1);
-  if (nkt > 1) {
-    async_tile(kseg, 1, kbuf1, 0);
-    async_bias(1, bbuf1);
+  // K tile 1 unconditionally (tile 0 again when it is the only one), so that the number of
+  // copies in flight after K tile 0 is the same on every path.
+  async_tile(kseg, min(1, nkt - 1), kbuf1, 0);
+  async_bias(min(1, nkt - 1), bbuf1);
+  // Q in the B-operand layout, and the diagonal term's initial state.
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int64_t t = wrow0 + qb * 16 + l16;
+    const bool valid = t < row_end;
+    float dot = 0.f;
+    // The diagonal term belongs to one piece of a split item only.
+    const bool self = !INPLACE && a.diag && valid && piece == 0 && !token_kept(a.g, t);  // (no G2F row has one)
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc) {
+      const uint4 raw = qraw[qb][cc];
+      uint4 kraw = make_uint4(0, 0, 0, 0);
+      if (self) kraw = *reinterpret_cast<const uint4*>(Kin + size_t(t) * kHeadDim + cc * 32 + grp * 8);
+      const uint32_t qw[4] = {raw.x, raw.y, raw.z, raw.w};
+      const uint32_t kw[4] = {kraw.x, kraw.y, kraw.z, kraw.w};
+      bf16x8_t v;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float q0 = __uint_as_float(qw[i] << 16) * qscale, q1 = __uint_as_float(qw[i] & 0xffff0000u) * qscale;
+        v[2 * i] = (__bf16)q0;
+        v[2 * i + 1] = (__bf16)q1;
+        // Diagonal self logit from the same scaled query the matrix core uses.
+        dot = fmaf(float(v[2 * i]), __uint_as_float(kw[i] << 16), dot);
+        dot = fmaf(float(v[2 * i + 1]), __uint_as_float(kw[i] & 0xffff0000u), dot);
+      }
+      qf[qb][cc] = v;
+    }
+    // Diagonal term: a query whose own token is not in S starts with its self term
+    // (m = self logit, weight 2^-w in l and O); the others start empty.
+    dot = group_sum(dot);
+    if constexpr (LOGSIZE) {
+      if (self) dot += a.logsize[t] * a.size_scale;
+    }
+    m_run[qb] = self ? dot : -INFINITY;
+    l_run[qb] = (self && grp == 0) ? shift_scale : 0.f;
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      f32x4_t init = {0.f, 0.f, 0.f, 0.f};
+      if (self) {
+        const uint2 vr = *reinterpret_cast<const uint2*>(Vin + size_t(t) * kHeadDim + db * 16 + grp * 4);
+        init[0] = __uint_as_float(vr.x << 16) * shift_scale;
+        init[1] = __uint_as_float(vr.x & 0xffff0000u) * shift_scale;
+        init[2] = __uint_as_float(vr.y << 16) * shift_scale;
+        init[3] = __uint_as_float(vr.y & 0xffff0000u) * shift_scale;
+      }
+      o[qb][db] = init;
+    }
   }
-  wait_tiles();
-  __syncthreads();
+  // Only K tile 0 (and its biases) is needed for the first scores: wait for the copies before the
+  // ones issued after it (V tile 0, K tile 1 and its biases: 2 + 2 loads per wave, one more for
+  // wave 0 under size-aware keys; vector-memory loads complete in issue order), so that those
+  // land while tile 0 is scored.  A bare barrier, since __syncthreads' release fence would wait
+  // for every copy; the memory clobber keeps LDS reads below it.
+  if (LOGSIZE && wave == 0) __builtin_amdgcn_s_waitcnt(kWaitVmcnt0 | 5);
+  else __builtin_amdgcn_s_waitcnt(kWaitVmcnt0 | 4);
+  asm volatile("s_barrier" ::: "memory");
 
   // One pipelined step: finish tile j (scores s_cur) while the scores of tile j+1 are formed,
   // query block by query block so that every stretch of code mixes matrix-core and VALU work.
@@ -530,15 +548,21 @@ void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const float m_new = vmax(m_run[qb], row_max(sa[qb]));  // finite: tile 0 holds a valid key
-    const float alpha = __builtin_amdgcn_exp2f((m_run[qb] - m_new) * sc);
+    if constexpr (!INPLACE) {  // (without a diagonal term l and O are still zero)
+      const float alpha = __builtin_amdgcn_exp2f((m_run[qb] - m_new) * sc);
+      l_run[qb] *= alpha;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) o[qb][k] *= alpha;
+    }
     m_run[qb] = m_new;
-    l_run[qb] *= alpha;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      o[qb][k] *= alpha;
       if constexpr (PRESCALE_Q) sa[qb][k] -= m_new;
     }
   }
+  // V tile 0 and K tile 1 for the first step.
+  wait_tiles();
+  __syncthreads();
   int j = 0;  // always even at the top of these loops
   for (; j + 2 < nkt && j + 2 < slow_from; j += 2) {
     step(even_t{}, plain_t{}, j, sa, sb);
@@ -574,7 +598,7 @@ void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const float l = group_sum(l_run[qb]);
-    const float inv = 1.f / l;
+    const float inv = __builtin_amdgcn_rcpf(l);
     const int64_t t = wrow0 + qb * 16 + l16;
     if (t >= row_end) continue;
 #pragma unroll
