@@ -11,11 +11,14 @@
 //
 // attn_bf16_kernel: flash-style forward on the bf16 matrix cores (v_mfma_f32_16x16x32_bf16,
 // float32 accumulation).  A work-group of 4 waves owns BM = 4*16*QB query rows of one head and
-// streams the key segment in 64-key tiles through LDS filled by direct global->LDS copies.
-// Scores are formed transposed, S^T = K Q^T, so each lane holds 4 keys x 1 query per 16x16
-// block: the row max is a 16-value in-lane max plus two cross-lane steps, the row sum stays
-// lane-local until the epilogue, and the bf16 probabilities are already laid out as the B
-// operand of O^T = V^T P^T (the packed value tiles store keys in the matching order).
+// streams the key segment -- the packed workspace, or under G2F the frame's own rows of K and
+// V read in place -- in 64-key tiles through LDS filled by direct global->LDS buffer loads.
+// Work items are numbered XCD by XCD, so that neighbouring items share an L2.  Scores are
+// formed transposed, S^T = K Q^T, so each lane holds 4 keys x 1 query per 16x16 block: the row
+// max is a 16-value in-lane max plus two cross-lane steps, the row sum stays lane-local until
+// the epilogue, and the bf16 probabilities are already laid out as the B operand of
+// O^T = V^T P^T (packed value tiles store keys in the matching order; in-place value tiles are
+// read transposed out of LDS in that order).
 //
 // attn_f32_kernel: float32 path (fp32 inputs and outputs), one lane per query, keys through LDS.
 #include <hip/hip_runtime.h>
