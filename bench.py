@@ -183,6 +183,19 @@ def time_calls(plans, tensors, outs, wss, steps, warmup):
     return wall, attn
 
 
+def attention_entry(d, secs, flops, plan) -> dict:
+    """One form's attention-stage time against its roofline: the bf16 MFMA peak, or for G2M (a
+    broadcast of the mean value: out = v-bar, nothing to multiply) HBM bandwidth on its output
+    writes."""
+    e = {"form": form_name(d), "ms": secs * 1e3, "kv_tokens": plan.counts()["n_kv"],
+         "tflops": flops / secs / 1e12, "frac_bf16_peak": flops / secs / 1e12 / MFMA_BF16_PEAK_TFLOPS}
+    if d.get("g2m"):
+        out_bytes = plan.T * d["heads"] * 64 * 4
+        e.update({"bound": "hbm", "out_bytes": out_bytes, "GB/s": out_bytes / secs / 1e9,
+                  "frac_hbm_peak": out_bytes / secs / 1e9 / HBM_PEAK_GBS})
+    return e
+
+
 def timed_group(dev, name, descs, dtype, tensors, steps):
     """Time the forwards of one group of plans on shared tensors; one result entry."""
     import torch
@@ -203,9 +216,7 @@ def timed_group(dev, name, descs, dtype, tensors, steps):
     T = plans[0].T
     entry = {"name": name, "ms_per_step": wall * 1e3, "queries_per_s": T / wall,
              "tflops": sum(flops) / wall / 1e12, "pct_bf16_peak": 100 * sum(flops) / wall / 1e12 / MFMA_BF16_PEAK_TFLOPS,
-             "attention": [{"form": form_name(d), "ms": a * 1e3, "kv_tokens": p.counts()["n_kv"],
-                            "tflops": f / a / 1e12, "frac_bf16_peak": f / a / 1e12 / MFMA_BF16_PEAK_TFLOPS}
-                           for d, a, f, p in zip(descs, attn, flops, plans)]}
+             "attention": [attention_entry(d, a, f, p) for d, a, f, p in zip(descs, attn, flops, plans)]}
     log(f"extra {name}: {wall * 1e3:.3f} ms/step, {entry['tflops']:.1f} TFLOP/s")
     del outs, wss
     torch.cuda.empty_cache()

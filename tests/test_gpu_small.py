@@ -73,7 +73,10 @@ def test_parity_bf16(lib, desc, label):
     assert_close(got, ref, fp32=False, label=label)
 
 
-@pytest.mark.parametrize("desc,label", CASES[:6], ids=[c[1] for c in CASES[:6]])
+BF16_OUT = CASES[:6] + [NEW["g2m"]]
+
+
+@pytest.mark.parametrize("desc,label", BF16_OUT, ids=[c[1] for c in BF16_OUT])
 def test_parity_bf16_out(lib, desc, label):
     q, k, v = inputs_for(desc, "bf16", seed=3)
     _, got, _, _ = run(lib, desc, q, k, v, out_dtype="bf16")

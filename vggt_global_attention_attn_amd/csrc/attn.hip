@@ -23,6 +23,7 @@
 // attn_f32_kernel: float32 path (fp32 inputs and outputs), one lane per query, keys through LDS.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <type_traits>
 
@@ -745,11 +746,57 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
   }
 }
 
+// G2M: every query attends to the one mean key, so its softmax weight is exactly 1 and each
+// output row is the mean value itself -- what the general kernel computes too (p = 2^0 = 1,
+// O = 1 * v, l = 1), bit for bit.  So the output is a broadcast of v-bar[h] to every row of head
+// h: each thread writes 16-byte chunks of one fixed column range (the grid stride is a multiple
+// of the chunks per row), and the kernel is bound by the output writes.
+template <typename E, bool OUT_BF16>
+__global__ __launch_bounds__(256) void g2m_broadcast_kernel(const E* means, void* out, int64_t T) {
+  constexpr int PER = OUT_BF16 ? 8 : 4;    // output elements per 16-byte chunk
+  constexpr int CPR = kHeadDim / PER;      // chunks per row
+  static_assert(256 % CPR == 0, "the grid stride must keep each thread on one column range");
+  const int h = blockIdx.y;
+  const E* vbar = means + (size_t(h) * 2 + 1) * kHeadDim;  // means[h][0][1][:]
+  const int64_t total = T * CPR;
+  const int64_t stride = int64_t(gridDim.x) * 256;
+  int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  const int col = int(i % CPR) * PER;
+  uint4 chunk;
+  if constexpr (OUT_BF16) {
+    static_assert(sizeof(E) == 2, "bf16 output comes from bf16 input");
+    chunk = *reinterpret_cast<const uint4*>(vbar + col);
+  } else {
+    float f[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if constexpr (sizeof(E) == 2) f[j] = __uint_as_float(uint32_t(vbar[col + j]) << 16);
+      else f[j] = vbar[col + j];
+    }
+    chunk = make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]), __float_as_uint(f[3]));
+  }
+  uint4* dst = reinterpret_cast<uint4*>(static_cast<char*>(out) + size_t(h) * size_t(T) * kHeadDim * (OUT_BF16 ? 2 : 4));
+  for (; i < total; i += stride) dst[i] = chunk;
+}
+
 }  // namespace
 
 hipError_t launch_attend(const vggt_attn_plan_s& p, const void* q, const void* k, const void* v,
                          void* out, void* ws, hipStream_t stream) {
   char* base = static_cast<char*>(ws);
+  if (p.g2m) {
+    const bool ob = p.out_dtype == VGGT_ATTN_BF16;
+    const int64_t total = p.T * (ob ? kHeadDim / 8 : kHeadDim / 4);
+    const dim3 grid(unsigned(std::min<int64_t>((total + 255) / 256, 1024)), unsigned(p.heads));
+    const void* means = base + p.layout.off_means;
+    if (p.in_dtype == VGGT_ATTN_FP32)
+      hipLaunchKernelGGL((g2m_broadcast_kernel<float, false>), grid, dim3(256), 0, stream, static_cast<const float*>(means), out, p.T);
+    else if (ob)
+      hipLaunchKernelGGL((g2m_broadcast_kernel<uint16_t, true>), grid, dim3(256), 0, stream, static_cast<const uint16_t*>(means), out, p.T);
+    else
+      hipLaunchKernelGGL((g2m_broadcast_kernel<uint16_t, false>), grid, dim3(256), 0, stream, static_cast<const uint16_t*>(means), out, p.T);
+    return hipGetLastError();
+  }
   AttnArgs a{};
   a.q = q;
   a.k = k;
