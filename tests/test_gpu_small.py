@@ -73,7 +73,9 @@ def test_parity_bf16(lib, desc, label):
     assert_close(got, ref, fp32=False, label=label)
 
 
-BF16_OUT = CASES[:6] + [NEW["g2m"]]
+# bf16 output on every kernel form: the general kernel, split work items merged by the merge kernel
+# (dense-37x37: 44 items on 512 slots), G2F read in place (g2f-37x37, also split) and G2M.
+BF16_OUT = CASES[:6] + [CASES[8], CASES[9], NEW["g2m"]]
 
 
 @pytest.mark.parametrize("desc,label", BF16_OUT, ids=[c[1] for c in BF16_OUT])
