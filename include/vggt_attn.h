@@ -53,7 +53,7 @@ extern "C" {
 typedef enum {
   VGGT_ATTN_OK = 0,
   VGGT_ATTN_EINVAL = -1,       /* invalid argument or descriptor                          */
-  VGGT_ATTN_EUNSUPPORTED = -2, /* valid request this build does not implement (head_dim) */
+  VGGT_ATTN_EUNSUPPORTED = -2, /* valid request the library does not implement (head_dim) */
   VGGT_ATTN_ENOSPC = -3,       /* workspace smaller than vggt_attn_workspace_bytes()      */
   VGGT_ATTN_EALIGN = -4,       /* a device pointer is not 16-byte aligned                 */
   VGGT_ATTN_EALIAS = -5,       /* out overlaps q, k, v or the workspace                   */

@@ -11,7 +11,7 @@
 
 namespace vggt {
 
-constexpr int kHeadDim = 64;   // the only head size this build implements
+constexpr int kHeadDim = 64;   // the only head size the library implements
 constexpr int kTile = 64;      // packed key rows per tile (attention key-tile height)
 constexpr int64_t kMaxTokens = 8000000;
 constexpr int kMaxHeads = 4096;
