@@ -103,7 +103,8 @@ class Sized:
     def pack(self, k, v, ws):
         self.plan.pack_sized(k, v, self.log_g, ws)
 
-KERNEL_SOURCES = ("vggt_global_attention_attn_amd/csrc/attn.hip", "vggt_global_attention_attn_amd/csrc/device_common.h")
+KERNEL_SOURCES = ("vggt_global_attention_attn_amd/csrc/attn.hip", "vggt_global_attention_attn_amd/csrc/device_common.h",
+                  "vggt_global_attention_attn_amd/csrc/plan.h")
 TRAFFIC_FILE = "profiles/attn_{workload}_hbm_traffic.txt"
 
 
