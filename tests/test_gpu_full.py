@@ -7,7 +7,8 @@ COUNT means); G2F, SGA sigma 9, and sigma 9 with the phase-shifted grid and a gl
 mean on the same 200-frame tensors; SGA sigma 6 at 800 frames, with and without the phase
 shift.  All use 37x37 patches + 5 special tokens per frame, 16 heads, d = 64, bf16 inputs and
 fp32 output.  One gives every token a seeded group size of 1..4 (size-aware keys); the last runs
-G2F at the largest token count a plan accepts."""
+G2F at the largest token count a plan accepts.  A separate test runs the 800-frame sigma 6
+workload on the tied-Q/K stress input with bf16 output."""
 import numpy as np
 import pytest
 
@@ -83,3 +84,32 @@ def test_full_size_sampled_rows(name, desc):
     ref = oracle.attention(q, k, v, desc, rows=rows, workers=host_threads(), log_g=log_g)
     print(f"[full] {name}: max-abs %.3e rel-L2 %.3e" % errors(got, ref), flush=True)
     assert_close(got, ref, fp32=False, label=name)
+
+
+@pytest.mark.timeout(900)
+def test_full_size_tied_qk_bf16_out():
+    """The 800-frame sigma 6 workload on the tied-Q/K stress input (K carries Q's per-position
+    component, so every query's logits peak at its own slot in all 800 frames and the running max
+    moves across the whole key range), with bf16 output, on the 4096 sampled rows."""
+    import torch
+    import vggt_global_attention_attn_amd as va
+    desc = Desc(800, 37, 37, 16, sigma=6, diag=True, mean=True)
+    _cache.clear()
+    print("[full] tied-qk: drawing inputs", flush=True)
+    q, k, v = make_qkv(desc.frames, desc.grid_h, desc.grid_w, desc.n_special, desc.heads, desc.head_dim,
+                       "bf16", seed=0, tie_qk=True)
+    up = lambda x: torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda()
+    plan = va.Plan(**plan_kwargs(desc, out_dtype="bf16"))
+    out = plan.new_output()
+    ws = plan.new_workspace()
+    print("[full] tied-qk: pack + attend", flush=True)
+    plan.forward(up(q), up(k), up(v), out, ws)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(out.float()).all())
+    rows = sample_rows(desc.frames, desc.grid_h, desc.grid_w, desc.n_special, count=4096, seed=1)
+    got = out[:, torch.from_numpy(rows).cuda()].double().cpu().numpy()
+    del out, ws
+    print(f"[full] tied-qk: oracle on {rows.size} rows", flush=True)
+    ref = oracle.attention(q, k, v, desc, rows=rows, workers=host_threads())
+    print("[full] tied-qk: max-abs %.3e rel-L2 %.3e" % errors(got, ref), flush=True)
+    assert_close(got, ref, fp32=False, label="tied-qk-800f-bf16-out")
