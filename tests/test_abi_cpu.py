@@ -180,7 +180,7 @@ def test_token_limit_is_exact(va):
 
 def test_split_cases_split(va):
     """The GPU cases meant to exercise split work items do split: dense 3x37x37 (44 items on 512
-    slots: 8 pieces each) and G2F 4x37x37 (88 items: 5 pieces of 22 tiles); the 800-frame
+    slots: 8 pieces each) and G2F 4x37x37 (64 items: 5 pieces of 22 tiles); the 800-frame
     workload (91,600 items) does not."""
     assert va.Plan(3, 37, 37, 2, sigma=1).layout()["split_pieces"] == 8
     assert va.Plan(4, 37, 37, 2, g2f=True).layout()["split_pieces"] == 5

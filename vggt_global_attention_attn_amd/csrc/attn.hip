@@ -495,6 +495,24 @@ void attn_bf16_kernel(AttnArgs a) {
   else __builtin_amdgcn_s_waitcnt(kWaitVmcnt0 | 4);
   asm volatile("s_barrier" ::: "memory");
 
+  // A wave with no query row in range (in the last, partial work item of a frame or a head)
+  // computes nothing: it only copies its share of every tile and meets every barrier of the
+  // steps below (one after tile 0, one per step), leaving its SIMD to the other work-group's
+  // wave.  (Wave 0 always has rows, so the bias copies of wave 0 never take this path.)
+  if (wrow0 >= row_end) {
+    wait_tiles();
+    __syncthreads();
+    for (int jj = 0; jj + 1 < nkt; ++jj) {
+      const bool odd = jj & 1;
+      async_tile(kseg, min(jj + 2, nkt - 1), odd ? kbuf1 : kbuf0, 0);
+      async_bias(min(jj + 2, nkt - 1), odd ? bbuf1 : bbuf0);
+      async_tile(vseg, jj + 1, odd ? vbuf0 : vbuf1, 1);
+      wait_tiles();
+      __syncthreads();
+    }
+    return;
+  }
+
   // One pipelined step: finish tile j (scores s_cur) while the scores of tile j+1 are formed,
   // query block by query block so that every stretch of code mixes matrix-core and VALU work.
   // P = j & 1 is a compile-time constant, so every LDS buffer is static.  MASK = tile j+1 may

@@ -28,7 +28,7 @@ constexpr int kMaxPhases = 9;  // s_h * s_w for the largest window (3 x 3)
 #define VGGT_GLOBAL_WPE 2
 #endif
 #ifndef VGGT_G2F_QB
-#define VGGT_G2F_QB 2
+#define VGGT_G2F_QB 3
 #endif
 #ifndef VGGT_G2F_WPE
 #define VGGT_G2F_WPE 2
