@@ -83,15 +83,39 @@ __global__ __launch_bounds__(256) void means_kernel(MeansArgs a) {
   float ks[CH], vs[CH];
 #pragma unroll
   for (int i = 0; i < CH; ++i) ks[i] = vs[i] = 0.f;
-  for (int j = rg; j < a.g.L; j += RG) {
-    if (!a.g.g2m) {
-      if (j < a.g.n_special) continue;  // specials are always kept
-      const int p = j - a.g.n_special;
-      const int r = p / a.g.grid_w, c = p - r * a.g.grid_w;
-      if (patch_kept(a.g, k, r, c)) continue;  // kept: not part of D_f
+  // Rows in batches of U per thread: every load of a batch is issued before the first add, so
+  // 2*U 16-byte loads are in flight per thread (kept rows and rows past the frame load nothing).
+  constexpr int U = 4;
+  for (int j0 = rg; j0 < a.g.L; j0 += RG * U) {
+    uint4 kr[U], vr[U];
+    bool use[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int j = j0 + u * RG;
+      bool dropped = j < a.g.L;
+      if (!a.g.g2m && dropped) {
+        if (j < a.g.n_special) {
+          dropped = false;  // specials are always kept
+        } else {
+          const int p = j - a.g.n_special;
+          const int r = p / a.g.grid_w, c = p - r * a.g.grid_w;
+          dropped = !patch_kept(a.g, k, r, c);  // kept: not part of D_f
+        }
+      }
+      use[u] = dropped;
+      kr[u] = vr[u] = make_uint4(0, 0, 0, 0);
+      if (dropped) {
+        kr[u] = *reinterpret_cast<const uint4*>(kb + size_t(j) * kHeadDim);
+        vr[u] = *reinterpret_cast<const uint4*>(vb + size_t(j) * kHeadDim);
+      }
     }
-    add_chunk<E>(ks, *reinterpret_cast<const uint4*>(kb + size_t(j) * kHeadDim));
-    add_chunk<E>(vs, *reinterpret_cast<const uint4*>(vb + size_t(j) * kHeadDim));
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (use[u]) {
+        add_chunk<E>(ks, kr[u]);
+        add_chunk<E>(vs, vr[u]);
+      }
+    }
   }
   __shared__ float red[RG][2][kHeadDim];
 #pragma unroll
