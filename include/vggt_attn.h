@@ -71,11 +71,17 @@ enum {
   VGGT_ATTN_DIAG = 1u << 2,       /* diagonal self term for queries whose token is not in S    */
   VGGT_ATTN_MEAN = 1u << 3,       /* one mean K/V per compressed frame, over its dropped patches */
   VGGT_ATTN_MEAN_COUNT = 1u << 4, /* mean logit += ln|D_f|, else the mean is one plain token    */
-  VGGT_ATTN_PRESCALE_Q = 1u << 5, /* bf16 path only: scale Q by tau*log2(e) once and round it to
-                                     bf16, saving one multiply per score (about 8% faster).  Every
-                                     logit of a row then carries a coherent relative error of up to
-                                     2^-9; without the flag Q is used exactly as given.  Ignored for
-                                     fp32 inputs.                                                  */
+  VGGT_ATTN_PRESCALE_Q = 1u << 5, /* bf16 path: fold the softmax scale into Q and form Q K^T on
+                                     the f16 matrix cores.  The pack stage converts the packed keys
+                                     of head h to f16 after scaling them by 2^-e_h, where e_h puts
+                                     the head's largest packed |k| in [128, 256) (exact for every
+                                     |k| above 2^-22 of that maximum); the attention stage rounds
+                                     Q * tau * log2(e) * 2^e_h to f16 once.  Saves one multiply
+                                     per score (about 8% faster); each logit term then carries a
+                                     relative error of up to 2^-11.  Without the flag Q and K are
+                                     used exactly as given and the scale is applied in float32.
+                                     G2F plans with the flag pack K and V like the global forms.
+                                     Ignored for fp32 inputs and with LOG_SIZE.                    */
   VGGT_ATTN_PHASE_SHIFT = 1u << 6, /* SGA grid of frame f offset by row (f div s_w) mod s_h and
                                      column f mod s_w (RegimeVGGT notes, 关键设计 3, whose t x t
                                      formula this is for square windows): frame f keeps patch
@@ -115,11 +121,15 @@ typedef struct {
                                 output) of the key-range pieces of a split last round of
                                 work-groups, merged before the call returns (bf16 inputs)     */
   int64_t split_pieces;      /* key-range pieces per work item of that round (0 = no split)   */
-  int64_t off_kpack;         /* [H][segments*segment_rows][d] input dtype                    */
+  int64_t off_kmax;          /* uint32 [H]: bf16 bits of the largest |k| among the packed keys
+                                of each head, which sets the f16 key scale (PRESCALE_Q only) */
+  int64_t off_kpack;         /* [H][segments*segment_rows][d] input dtype (PRESCALE_Q: f16,
+                                each head's rows scaled by 2^-e_h, see the flag)              */
   int64_t off_vpack;         /* bf16: [H][rows/64][d][64] key-minor tiles (see below);
                                 fp32: [H][rows][d].  Both parts are empty (off_kpack ==
-                                off_vpack == total_bytes) for bf16 G2F plans, whose attention
-                                stage reads k and v directly (a frame's keys are its tokens) */
+                                off_vpack == total_bytes) for bf16 G2F plans without
+                                PRESCALE_Q, whose attention stage reads k and v directly (a
+                                frame's keys are its tokens)                                  */
   int64_t total_bytes;
 } vggt_attn_layout_t;
 

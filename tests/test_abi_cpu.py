@@ -84,12 +84,12 @@ def test_plan_counts_match_oracle(va, desc):
     assert c["flops"] == pytest.approx(flops, rel=1e-12)
     lay = p.layout()
     assert lay["segment_rows"] % 64 == 0 and lay["segment_rows"] >= lay["keys_per_segment"]
-    for key in ("off_index", "off_dcount", "off_means", "off_partial", "off_kbias", "off_logsize", "off_kpack",
-                "off_vpack", "total_bytes"):
+    for key in ("off_index", "off_dcount", "off_means", "off_partial", "off_kbias", "off_logsize", "off_kmax",
+                "off_kpack", "off_vpack", "total_bytes"):
         assert lay[key] % 256 == 0
     if desc.log_size:
         assert lay["off_logsize"] - lay["off_kbias"] >= 4 * lay["segments"] * lay["segment_rows"]
-        assert lay["off_kpack"] - lay["off_logsize"] >= 4 * desc.T
+        assert lay["off_kmax"] - lay["off_logsize"] >= 4 * desc.T
     assert lay["total_bytes"] == p.workspace_bytes
     # The packed parts hold H x padded rows x d values, except for bf16 G2F plans, whose keys
     # (each frame's own tokens) are read in place.
@@ -185,3 +185,18 @@ def test_split_cases_split(va):
     assert va.Plan(3, 37, 37, 2, sigma=1).layout()["split_pieces"] == 8
     assert va.Plan(4, 37, 37, 2, g2f=True).layout()["split_pieces"] == 5
     assert va.Plan(800, 37, 37, 16, sigma=6, diag=True, mean=True).layout()["split_pieces"] == 0
+    assert va.Plan(3, 37, 37, 2, sigma=1, prescale_q=True).layout()["split_pieces"] == 8
+
+
+def test_f16_score_form_layout(va):
+    """PRESCALE_Q (f16 score form): a uint32 key maximum per head, and G2F plans keep a packed
+    copy (their f16 keys cannot be read in place); fp32 plans ignore the flag."""
+    for kw in (dict(sigma=6, diag=True, mean=True), dict(sigma=1), dict(g2f=True)):
+        lay = va.Plan(4, 13, 11, 3, prescale_q=True, **kw).layout()
+        rows = lay["segments"] * lay["segment_rows"]
+        assert lay["off_kmax"] % 256 == 0 and lay["off_kpack"] - lay["off_kmax"] >= 3 * 4
+        assert lay["off_vpack"] - lay["off_kpack"] >= 3 * rows * 64 * 2
+        plain = va.Plan(4, 13, 11, 3, **kw).layout()
+        assert plain["off_kpack"] == plain["off_kmax"]
+    lay = va.Plan(4, 13, 11, 3, sigma=4, prescale_q=True, in_dtype="fp32").layout()
+    assert lay["off_kpack"] == lay["off_kmax"]

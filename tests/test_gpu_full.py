@@ -7,7 +7,8 @@ COUNT means); G2F, SGA sigma 9, and sigma 9 with the phase-shifted grid and a gl
 mean on the same 200-frame tensors; SGA sigma 6 at 800 frames, with and without the phase
 shift.  All use 37x37 patches + 5 special tokens per frame, 16 heads, d = 64, bf16 inputs and
 fp32 output.  One gives every token a seeded group size of 1..4 (size-aware keys); the last runs
-G2F at the largest token count a plan accepts.  A separate test runs the 800-frame sigma 6
+G2F at the largest token count a plan accepts.  Names ending in -f16 run the f16 score form
+(PRESCALE_Q: packed keys f16(k * 2^-e_h), Q * tau * log2(e) * 2^e_h rounded to f16 once).  A separate test runs the 800-frame sigma 6
 workload on the tied-Q/K stress input with bf16 output."""
 import numpy as np
 import pytest
@@ -21,14 +22,17 @@ pytestmark = pytest.mark.gpu
 
 FULL = [
     ("dense-32f", Desc(32, 37, 37, 16, sigma=1)),
+    ("dense-32f-f16", Desc(32, 37, 37, 16, sigma=1)),
     ("g2m-32f", Desc(32, 37, 37, 16, g2m=True)),
     ("sga4-100f", Desc(100, 37, 37, 16, sigma=4, diag=True, mean=True)),
     ("sga4-100f-count", Desc(100, 37, 37, 16, sigma=4, diag=True, mean=True, mean_count=True)),
     ("g2f-200f", Desc(200, 37, 37, 16, g2f=True)),
+    ("g2f-200f-f16", Desc(200, 37, 37, 16, g2f=True)),
     ("sga9-200f", Desc(200, 37, 37, 16, sigma=9, diag=True, mean=True)),
     ("sga9-200f-phase-global-count", Desc(200, 37, 37, 16, sigma=9, diag=True, mean=True, mean_count=True,
                                           phase_shift=True, mean_global=True)),
     ("sga6-800f", Desc(800, 37, 37, 16, sigma=6, diag=True, mean=True)),
+    ("sga6-800f-f16", Desc(800, 37, 37, 16, sigma=6, diag=True, mean=True)),
     ("sga6-800f-phase", Desc(800, 37, 37, 16, sigma=6, diag=True, mean=True, phase_shift=True)),
     ("sga6-800f-sized", Desc(800, 37, 37, 16, sigma=6, diag=True, log_size=True)),
     # the largest plan the library accepts: T = 7,999,428 tokens (limit 8,000,000); with 6 heads
@@ -59,7 +63,8 @@ def test_full_size_sampled_rows(name, desc):
     import vggt_global_attention_attn_amd as va
     print(f"[full] {name}: drawing inputs", flush=True)
     (q, k, v), (qd, kd, vd) = device_inputs(desc)
-    plan = va.Plan(**plan_kwargs(desc))
+    # "-f16": the f16 score form (PRESCALE_Q)
+    plan = va.Plan(**plan_kwargs(desc), prescale_q=name.endswith("-f16"))
     out = plan.new_output()
     ws = plan.new_workspace()
     print(f"[full] {name}: pack + attend", flush=True)

@@ -52,9 +52,9 @@ def lib():
     return va
 
 
-def run(va, desc, q, k, v, out_dtype="fp32", in_dtype="bf16"):
+def run(va, desc, q, k, v, out_dtype="fp32", in_dtype="bf16", prescale_q=False):
     import torch
-    plan = va.Plan(**plan_kwargs(desc, in_dtype, out_dtype))
+    plan = va.Plan(**plan_kwargs(desc, in_dtype, out_dtype), prescale_q=prescale_q)
     qd, kd, vd = to_device(q), to_device(k), to_device(v)
     out = plan.new_output()
     ws = plan.new_workspace()
@@ -245,36 +245,96 @@ def _rising(desc, seed, spike=None):
     (Desc(6, 13, 11, 2, sigma=4, diag=True, mean=True), "sga4-enh"),
     (Desc(4, 37, 37, 2, g2f=True), "g2f"),
 ], ids=["dense", "sga4-enh", "g2f"])
-def test_running_max_catch_up(lib, desc, label):
+@pytest.mark.parametrize("prescale_q", [False, True], ids=["exact", "f16"])
+def test_running_max_catch_up(lib, desc, label, prescale_q):
     """Logits that keep rising along the keys force the rare exact catch-up of the running max
     (a score more than an octave above it) in many tiles; a spiked key drives exp2 past the
-    float range before the catch-up.  Both must still match the oracle."""
+    float range before the catch-up.  Both must still match the oracle, in the exact and the
+    f16 score form."""
     q, k, v = _rising(desc, seed=11)
-    _, got, _, _ = run(lib, desc, q, k, v)
+    _, got, _, _ = run(lib, desc, q, k, v, prescale_q=prescale_q)
     ref = oracle.attention(q, k, v, desc, workers=4)
+    print(label, prescale_q, "rising max-abs %.3e rel-L2 %.3e" % errors(got, ref))
     assert_close(got, ref, fp32=False, label=label + "/rising")
     last_frame_token = desc.T - 3
     q, k, v = _rising(desc, seed=12, spike=(last_frame_token, 40.0))
-    _, got, _, _ = run(lib, desc, q, k, v)
+    _, got, _, _ = run(lib, desc, q, k, v, prescale_q=prescale_q)
     ref = oracle.attention(q, k, v, desc, workers=4)
+    print(label, prescale_q, "spike max-abs %.3e rel-L2 %.3e" % errors(got, ref))
     assert_close(got, ref, fp32=False, label=label + "/spike")
 
 
-PRESCALED = [CASES[i] for i in (2, 4, 5, 7, 9)] + [NEW["sga6-phase-count"], NEW["sga4-global-count-phase"]]
+# f16 score form (PRESCALE_Q): plain SGA, enhanced SGA (UNIT and COUNT means, pi^3), dense with
+# split work items (dense-37x37), G2F on packed f16 keys (g2f-37x37, also split), the phase
+# shift and the global mean, and G2M (one mean key).
+PRESCALED = [CASES[i] for i in (0, 1, 2, 4, 5, 6, 7, 8, 9)] + [NEW["sga6-phase-count"], NEW["sga4-global-count-phase"],
+                                                               NEW["sga2-phase-empty-sets"], NEW["g2m"]]
 
 
 @pytest.mark.parametrize("desc,label", PRESCALED, ids=[c[1] for c in PRESCALED])
-def test_parity_prescaled_q(lib, desc, label):
-    """The opt-in PRESCALE_Q form (Q scaled by tau*log2(e) and rounded to bf16 once) on the
-    seeded workload inputs."""
-    import torch
+@pytest.mark.parametrize("out_dtype", ["fp32", "bf16"])
+def test_parity_prescaled_q(lib, desc, label, out_dtype):
+    """The f16 score form: packed keys f16(k * 2^-e_h), Q * tau * log2(e) * 2^e_h rounded to
+    f16 once, on the seeded workload inputs."""
     q, k, v = inputs_for(desc, "bf16", seed=13)
-    plan = lib.Plan(**plan_kwargs(desc), prescale_q=True)
-    out = plan.new_output()
-    plan.forward(to_device(q), to_device(k), to_device(v), out, plan.new_workspace())
-    torch.cuda.synchronize()
+    _, got, _, _ = run(lib, desc, q, k, v, out_dtype=out_dtype, prescale_q=True)
     ref = oracle.attention(q, k, v, desc, workers=4)
-    assert_close(out.float().cpu().numpy(), ref, fp32=False, label=label + "/prescaled")
+    print(label, out_dtype, "f16 form max-abs %.3e rel-L2 %.3e" % errors(got, ref))
+    assert_close(got, ref, fp32=False, label=label + "/f16-" + out_dtype)
+
+
+def _key_exp(kmax_bits):
+    """The documented key-scale exponent: 2^-e puts the largest |k| in [128, 256)."""
+    if kmax_bits == 0:
+        return 0
+    km = np.array([kmax_bits << 16], dtype=np.uint32).view(np.float32)[0]
+    e = int(np.frexp(np.float64(km))[1]) - 8
+    return min(max(e, -120), 120)
+
+
+F16_PACKED = [CASES[5], CASES[8], CASES[9], NEW["sga4-global-count-phase"], NEW["g2m"]]
+
+
+@pytest.mark.parametrize("desc,label", F16_PACKED, ids=[c[1] for c in F16_PACKED])
+@pytest.mark.parametrize("scale", [1.0, 2.0 ** 20, 2.0 ** -30], ids=["k", "k*2^20", "k*2^-30"])
+def test_f16_packed_keys(lib, desc, label, scale):
+    """f16 score form: the per-head maximum is the largest |k| among the packed keys (S and the
+    means), and every packed key row is f16(k * 2^-e_h) exactly, e_h from that maximum; keys
+    scaled far from 1 (with Q scaled inversely, so the logits stay put) still match the oracle."""
+    import torch
+    from synth import bf16_bits_to_f32, f32_to_bf16_bits
+    q, k, v = inputs_for(desc, "bf16", seed=14)
+    if scale != 1.0:
+        k = f32_to_bf16_bits(bf16_bits_to_f32(k) * np.float32(scale))
+        q = f32_to_bf16_bits(bf16_bits_to_f32(q) / np.float32(scale))
+    plan, got, ws, _ = run(lib, desc, q, k, v, prescale_q=True)
+    lay = plan.layout()
+    H, d = desc.heads, desc.head_dim
+    rows = lay["segments"] * lay["segment_rows"]
+    kmax = ws[lay["off_kmax"]:lay["off_kmax"] + 4 * H].view(torch.int32).cpu().numpy().view(np.uint32)
+    kp = ws[lay["off_kpack"]:lay["off_kpack"] + H * rows * d * 2].view(torch.int16).cpu().numpy().view(np.uint16)
+    kp = kp.reshape(H, rows, d)
+    if desc.g2f:
+        src = [np.arange(f * desc.L, (f + 1) * desc.L) for f in range(desc.frames)]
+        seg = lay["segment_rows"]
+        packed_bf16 = np.zeros((H, rows, d), dtype=np.uint16)
+        for f, s_ in enumerate(src):
+            packed_bf16[:, f * seg:f * seg + s_.size] = k[:, s_]
+    else:
+        S = oracle.index_set(desc)
+        nS, M = S.size, lay["keys_per_segment"] - S.size
+        means = ws[lay["off_means"]:lay["off_means"] + H * M * 2 * d * 2].view(torch.int16).cpu().numpy()
+        means = means.view(np.uint16).reshape(H, M, 2, d)
+        packed_bf16 = np.zeros((H, rows, d), dtype=np.uint16)
+        packed_bf16[:, :nS] = k[:, S]
+        packed_bf16[:, nS:nS + M] = means[:, :, 0]
+    for h in range(H):
+        assert kmax[h] == int((packed_bf16[h] & 0x7FFF).max())
+        e = _key_exp(int(kmax[h]))
+        want = (bf16_bits_to_f32(packed_bf16[h]).astype(np.float64) * 2.0 ** -e).astype(np.float16).view(np.uint16)
+        assert np.array_equal(kp[h], want)
+    ref = oracle.attention(q, k, v, desc, workers=4)
+    assert_close(got, ref, fp32=False, label=f"{label}/f16-keys-x{scale:g}")
 
 
 SIZED = [
@@ -338,14 +398,15 @@ TIED = [(Desc(6, 13, 11, 2, sigma=6, diag=True, mean=True), "sga6-enh"),
 
 
 @pytest.mark.parametrize("desc,label", TIED, ids=[c[1] for c in TIED])
-def test_parity_tied_qk(lib, desc, label):
+@pytest.mark.parametrize("prescale_q", [False, True], ids=["exact", "f16"])
+def test_parity_tied_qk(lib, desc, label, prescale_q):
     """Stress input: K carries Q's per-position component, so a query's logits peak at its own
     patch position in every frame (about tau * 0.49 * 64 = 3.9 above the rest), far from the
     first tile's keys, which moves the running max."""
-    print(f"[tied] {label}", flush=True)
+    print(f"[tied] {label} {prescale_q}", flush=True)
     q, k, v = make_qkv(desc.frames, desc.grid_h, desc.grid_w, desc.n_special, desc.heads, desc.head_dim,
                        dtype="bf16", seed=21, tie_qk=True)
-    _, got, _, _ = run(lib, desc, q, k, v)
+    _, got, _, _ = run(lib, desc, q, k, v, prescale_q=prescale_q)
     ref = oracle.attention(q, k, v, desc, workers=4)
     print(label, "tied max-abs %.3e rel-L2 %.3e" % errors(got, ref))
     assert_close(got, ref, fp32=False, label=label + "/tied")

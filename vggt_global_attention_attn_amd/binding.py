@@ -33,7 +33,7 @@ class VggtAttnError(RuntimeError):
 class Layout(ctypes.Structure):
     _fields_ = [(name, ctypes.c_int64) for name in (
         "segments", "segment_rows", "keys_per_segment", "off_index", "off_dcount", "off_means",
-        "off_partial", "off_kbias", "off_logsize", "off_part", "split_pieces", "off_kpack", "off_vpack",
+        "off_partial", "off_kbias", "off_logsize", "off_part", "split_pieces", "off_kmax", "off_kpack", "off_vpack",
         "total_bytes")]
 
     def as_dict(self) -> dict:

@@ -35,6 +35,7 @@ namespace vggt {
 namespace {
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef short i16x8_t __attribute__((ext_vector_type(8)));
 // s_waitcnt immediate for vmcnt(0) with expcnt and lgkmcnt left at their maxima (gfx9 encoding).
@@ -64,7 +65,8 @@ struct AttnArgs {
   float mean_bias_s[kMaxPhases];     // raw-score units, ln(n)/tau (0 for UNIT weighting)
   float mean_bias_log2[kMaxPhases];  // the same in log2 units, log2(n) (PRESCALE_Q path)
   float c_log2;    // tau * log2(e)
-  float weight_shift, weight_scale;  // exact-scale weights are 2^-weight_shift (= weight_scale) smaller
+  float weight_shift, weight_scale;  // weights are 2^-weight_shift (= weight_scale) smaller
+  const uint32_t* kmax;  // f16 score form: bf16 bits of each head's largest packed |k|
   const float* kbias;    // size-aware keys: bias of each packed key row (raw-score units), else null
   const float* logsize;  // size-aware keys: log g per token (for the diagonal term), else null
   float size_scale;      // sqrt(d): log g -> raw-score units
@@ -145,7 +147,8 @@ template <int QB, int WPE, bool OUT_BF16, bool PRESCALE_Q, bool LOGSIZE, bool SP
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 void attn_bf16_kernel(AttnArgs a) {
   static_assert(!(LOGSIZE && PRESCALE_Q), "size-aware keys use the exact scale");
-  static_assert(!(SPLIT && (LOGSIZE || PRESCALE_Q)), "split pieces use the plain exact-scale form");
+  static_assert(!(SPLIT && LOGSIZE), "split pieces have no key biases");
+  static_assert(!(INPLACE && PRESCALE_Q), "the f16 score form reads f16 keys from the packed workspace");
   constexpr bool kExactScale = !PRESCALE_Q;
   constexpr int WQ = 16 * QB;  // query rows per wave
   constexpr int BM = 4 * WQ;   // query rows per work-group
@@ -216,23 +219,30 @@ void attn_bf16_kernel(AttnArgs a) {
   // Q as the B operand of S^T = K Q^T: lane (l16, grp) holds query l16 of its block and
   // channels cc*32 + grp*8 .. +7 for cc = 0, 1.
   bf16x8_t qf[QB][2];
-  float m_run[QB], l_run[QB];  // running max (raw scores; log2 units under PRESCALE_Q), lane-partial row sum
+  // Running max and lane-partial row sum.  From tile 0 on, the running max m is kept as the
+  // exp2 offset -(m + w) in log2 units (m c for raw scores s, plus the weight shift w below): the
+  // exact form adds it to c s in the exp argument, the f16 score form starts its QK^T chains
+  // from it.  Before tile 0 the slot holds the diagonal term's logit (raw or log2 units).
+  float m_run[QB], l_run[QB];
   f32x4_t o[QB][4];
   // Two ways to reach log2 units.  Exact (default): Q is used as given, scores and the running
   // max are in units of q.k, and the exp2 argument is multiplied by c = tau*log2(e).
-  // PRESCALE_Q (opt-in plan flag): Q is scaled by c once and rounded to bf16, which saves that
-  // multiply per score but perturbs every logit of a row by a relative 2^-9 -- coherently
-  // across the row, unlike the independent rounding of P.
+  // f16 score form (PRESCALE_Q plan flag): the packed keys of head h are f16(k * 2^-e_h) and Q
+  // is scaled by c * 2^e_h once and rounded to f16, so that the f16 matrix cores deliver scores
+  // in log2 units and the running max enters their accumulator: no multiply per score.  The
+  // rounding of Q perturbs each logit term by a relative 2^-11 at most.
   const float c = a.c_log2;
-  const float qscale = kExactScale ? 1.f : c;   // applied to Q at load
+  const int kexp = PRESCALE_Q ? key_scale_exp(a.kmax[h]) : 0;
+  const float qscale = kExactScale ? 1.f : __builtin_amdgcn_ldexpf(c, kexp);  // applied to Q at load
+  const float kscale = kExactScale ? 1.f : __builtin_amdgcn_ldexpf(1.f, -kexp);  // of the packed keys
   const float sc = kExactScale ? c : 1.f;       // applied to scores at the exp
-  // Weight shift w (exact mode, from the plan): every weight is taken 2^w times smaller,
+  // Weight shift w (from the plan): every weight is taken 2^w times smaller,
   // p = 2^(c (s - m) - w), a common factor that cancels in O / l (bf16 and fp32 keep the same
   // relative rounding while p stays far above 2^-126).  It moves the overflow test below from
   // one octave above the running max to w + 1 octaves, so the max that the first tile sets is
   // almost never raised.
-  const float shift = kExactScale ? a.weight_shift : 0.f;
-  const float shift_scale = kExactScale ? a.weight_scale : 1.f;  // 2^-w
+  const float shift = a.weight_shift;
+  const float shift_scale = a.weight_scale;  // 2^-w
   // Raw Q fragments of every query block, as straight-line range-checked buffer loads (rows
   // past the head's T read as zero; rows past the item's end are computed but never stored), so
   // that they are in flight together with the first tile copies issued below.
@@ -326,18 +336,24 @@ void attn_bf16_kernel(AttnArgs a) {
   // S^T = K Q^T for 64 keys x the 16 queries of block qb: s[k4][i] is key k4*16 + grp*4 + i.
   // Exact mode starts each two-MFMA chain from a zero accumulator (an inline constant, so the
   // first MFMA reads no accumulator registers and the second takes its input straight from the
-  // first); the running max is applied in the exp argument.  PRESCALE_Q mode starts it from
-  // -m, so the scores leave the matrix core already shifted.
+  // first); the running max is applied in the exp argument.  The f16 score form starts it from
+  // `from` = -(m + w), so the scores leave the matrix core already shifted.
   // Size-aware keys start the chain from the keys' biases instead (read from LDS).
-  auto scores_qb = [&](const bf16x8_t (&kf)[4][2], const float* bb, int qb, f32x4_t (&s)[4]) {
-    const float mneg = -m_run[qb];
+  auto scores_qb = [&](const bf16x8_t (&kf)[4][2], const float* bb, int qb, f32x4_t (&s)[4], float from) {
 #pragma unroll
     for (int k4 = 0; k4 < 4; ++k4) {
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-      if constexpr (PRESCALE_Q) acc = f32x4_t{mneg, mneg, mneg, mneg};
-      if constexpr (LOGSIZE) acc = *reinterpret_cast<const f32x4_t*>(bb + k4 * 16 + grp * 4);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[k4][0], qf[qb][0], acc, 0, 0, 0);
-      s[k4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[k4][1], qf[qb][1], acc, 0, 0, 0);
+      if constexpr (PRESCALE_Q) {
+        acc = f32x4_t{from, from, from, from};
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, kf[k4][0]),
+                                                     __builtin_bit_cast(f16x8_t, qf[qb][0]), acc, 0, 0, 0);
+        s[k4] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, kf[k4][1]),
+                                                       __builtin_bit_cast(f16x8_t, qf[qb][1]), acc, 0, 0, 0);
+      } else {
+        if constexpr (LOGSIZE) acc = *reinterpret_cast<const f32x4_t*>(bb + k4 * 16 + grp * 4);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[k4][0], qf[qb][0], acc, 0, 0, 0);
+        s[k4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[k4][1], qf[qb][1], acc, 0, 0, 0);
+      }
     }
   };
   // Mean-key bias and padding mask, only for the last tiles of the segment.
@@ -369,12 +385,12 @@ void attn_bf16_kernel(AttnArgs a) {
     y = fmaxf(fmaxf(y, s[3][1]), s[3][2]);
     return group_max(fmaxf(fmaxf(x, s[1][3]), fmaxf(y, s[3][3])));
   };
-  // p = 2^(c (s - m) - w) (exact) or 2^s' (PRESCALE_Q) rounded to bf16, already in the B-operand
-  // layout of the PV product; the row sum uses the same rounded weights.  Returns the OR of the
-  // packed bf16 words: every p >= 0, so some p >= 2 (a score more than w + 1 octaves above the
-  // running max) exactly when bit 14 of some half is set.
+  // p = 2^(c s - c m - w) (exact) or 2^s' (f16 score form, s' already offset) rounded to bf16,
+  // already in the B-operand layout of the PV product; the row sum uses the same rounded weights.
+  // Returns the OR of the packed bf16 words: every p >= 0, so some p >= 2 (a score more than
+  // w + 1 octaves above the running max) exactly when bit 14 of some half is set.
   auto probs_qb = [&](int qb, const f32x4_t (&s)[4], bf16x8_t (&pf)[2]) {
-    const float off = PRESCALE_Q ? 0.f : fmaf(-m_run[qb], c, -shift);
+    const float off = m_run[qb];
     auto e = [&](float x) { return (__bf16)__builtin_amdgcn_exp2f(PRESCALE_Q ? x : fmaf(x, c, off)); };
     uint32_t bits = 0;
     float l = l_run[qb];
@@ -407,17 +423,18 @@ void attn_bf16_kernel(AttnArgs a) {
   // rescaled) and the block redone, so in the steady state no per-score max and no rescale run.
   auto block = [&](const bf16x8_t (&kf)[4][2], const float* bb, int qb, f32x4_t (&s_cur)[4],
                    f32x4_t (&s_next)[4], bf16x8_t (&pf)[2], bool next) {
-    if (next) scores_qb(kf, bb, qb, s_next);
+    if (next) scores_qb(kf, bb, qb, s_next, m_run[qb]);
     const float l_prev = l_run[qb];
     const uint32_t bits = probs_qb(qb, s_cur, pf);
     if (__builtin_amdgcn_ballot_w64((bits & 0x40004000u) != 0) != 0) {
       asm volatile("; rare rescale" ::);  // keeps this branch from being speculated into every tile
-      // Exact mode: scores are absolute (q.k), d is the raise of m.  PRESCALE_Q: scores are
-      // relative to m (log2 units), so they and the already formed next-tile scores shift too.
+      // Exact mode: scores are absolute (q.k); the offset drops to -(c mx + w) for the row max
+      // mx.  f16 score form: scores are relative to m + w (log2 units), so the offset drops by
+      // the raise d of m, and the current and already formed next-tile scores shift with it.
       const float mx = row_max(s_cur);
-      const float d = PRESCALE_Q ? vmax(mx, 0.f) : vmax(mx - m_run[qb], 0.f);
-      const float alpha = __builtin_amdgcn_exp2f(-d * sc);
-      m_run[qb] += d;
+      const float d = PRESCALE_Q ? vmax(mx + shift, 0.f) : vmax(m_run[qb] - fmaf(-mx, c, -shift), 0.f);
+      const float alpha = __builtin_amdgcn_exp2f(-d);
+      m_run[qb] -= d;
       l_run[qb] = l_prev * alpha;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
@@ -453,21 +470,33 @@ void attn_bf16_kernel(AttnArgs a) {
       if (self) kraw = *reinterpret_cast<const uint4*>(Kin + size_t(t) * kHeadDim + cc * 32 + grp * 8);
       const uint32_t qw[4] = {raw.x, raw.y, raw.z, raw.w};
       const uint32_t kw[4] = {kraw.x, kraw.y, kraw.z, kraw.w};
-      bf16x8_t v;
+      if constexpr (PRESCALE_Q) {
+        f16x8_t v;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float q0 = __uint_as_float(qw[i] << 16) * qscale, q1 = __uint_as_float(qw[i] & 0xffff0000u) * qscale;
-        v[2 * i] = (__bf16)q0;
-        v[2 * i + 1] = (__bf16)q1;
-        // Diagonal self logit from the same scaled query the matrix core uses.
-        dot = fmaf(float(v[2 * i]), __uint_as_float(kw[i] << 16), dot);
-        dot = fmaf(float(v[2 * i + 1]), __uint_as_float(kw[i] & 0xffff0000u), dot);
+        for (int i = 0; i < 4; ++i) {
+          // (saturated at the f16 maximum: only logit terms beyond 2^22 octaves reach it)
+          const float q0 = __builtin_amdgcn_fmed3f(__uint_as_float(qw[i] << 16) * qscale, -65504.f, 65504.f);
+          const float q1 = __builtin_amdgcn_fmed3f(__uint_as_float(qw[i] & 0xffff0000u) * qscale, -65504.f, 65504.f);
+          v[2 * i] = (_Float16)q0;
+          v[2 * i + 1] = (_Float16)q1;
+          // Diagonal self logit from the same rounded query the matrix core uses (its key is
+          // scaled below, exactly as the packed keys are).
+          dot = fmaf(float(v[2 * i]), __uint_as_float(kw[i] << 16), dot);
+          dot = fmaf(float(v[2 * i + 1]), __uint_as_float(kw[i] & 0xffff0000u), dot);
+        }
+        qf[qb][cc] = __builtin_bit_cast(bf16x8_t, v);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {  // diagonal self logit, q.k in float32
+          dot = fmaf(__uint_as_float(qw[i] << 16), __uint_as_float(kw[i] << 16), dot);
+          dot = fmaf(__uint_as_float(qw[i] & 0xffff0000u), __uint_as_float(kw[i] & 0xffff0000u), dot);
+        }
+        qf[qb][cc] = __builtin_bit_cast(bf16x8_t, raw);
       }
-      qf[qb][cc] = v;
     }
     // Diagonal term: a query whose own token is not in S starts with its self term
     // (m = self logit, weight 2^-w in l and O); the others start empty.
-    dot = group_sum(dot);
+    dot = group_sum(dot) * kscale;
     if constexpr (LOGSIZE) {
       if (self) dot += a.logsize[t] * a.size_scale;
     }
@@ -559,12 +588,7 @@ void attn_bf16_kernel(AttnArgs a) {
     bf16x8_t kf[4][2];
     k_frags(kbuf0, kf);
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      const float m_self = m_run[qb];
-      m_run[qb] = 0.f;
-      scores_qb(kf, bbuf0, qb, sa[qb]);
-      m_run[qb] = m_self;
-    }
+    for (int qb = 0; qb < QB; ++qb) scores_qb(kf, bbuf0, qb, sa[qb], 0.f);
   }
   bias_mask(0, sa);
 #pragma unroll
@@ -576,10 +600,10 @@ void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
       for (int k = 0; k < 4; ++k) o[qb][k] *= alpha;
     }
-    m_run[qb] = m_new;
+    m_run[qb] = PRESCALE_Q ? -(m_new + shift) : fmaf(-m_new, c, -shift);
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      if constexpr (PRESCALE_Q) sa[qb][k] -= m_new;
+      if constexpr (PRESCALE_Q) sa[qb][k] -= m_new + shift;
     }
   }
   // V tile 0 and K tile 1 for the first step.
@@ -611,7 +635,7 @@ void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
       for (int db = 0; db < 4; ++db) *reinterpret_cast<f32x4_t*>(row + db * 16 + grp * 4) = o[qb][db];
       if (grp == 0) {
-        row[64] = m_run[qb];
+        row[64] = -m_run[qb];  // m + w in log2 units
         row[65] = l;
       }
     }
@@ -641,7 +665,7 @@ void attn_bf16_kernel(AttnArgs a) {
 // sums and unnormalised outputs combine exactly as the online softmax would have across the
 // whole key range.  One thread per (row, 4 channels); rows past the segment end are skipped.
 template <bool OUT_BF16>
-__global__ __launch_bounds__(256) void merge_pieces_kernel(AttnArgs a, int BM, float m_scale) {
+__global__ __launch_bounds__(256) void merge_pieces_kernel(AttnArgs a, int BM) {
   const int64_t gid = int64_t(blockIdx.x) * 256 + threadIdx.x;
   const int64_t rr = gid >> 4;  // row over all split items
   const int chunk = int(gid & 15);
@@ -658,7 +682,7 @@ __global__ __launch_bounds__(256) void merge_pieces_kernel(AttnArgs a, int BM, f
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
   for (int p = 0; p < a.nsplit; ++p) {
     const float* row = base + p * piece_stride;
-    const float e = __builtin_amdgcn_exp2f((row[64] - mx) * m_scale);
+    const float e = __builtin_amdgcn_exp2f(row[64] - mx);  // maxima in log2 units
     l = fmaf(row[65], e, l);
     acc += *reinterpret_cast<const f32x4_t*>(row + chunk * 4) * e;
   }
@@ -882,9 +906,9 @@ hipError_t launch_attend(const vggt_attn_plan_s& p, const void* q, const void* k
   // bf16: QB blocks of 16 query rows per wave, 4 waves per work-group, WPE work-groups'
   // waves per SIMD (occupancy), so that the matrix-core phase of one work-group overlaps the
   // softmax phase of another on the same CU.
-  constexpr int QBg = VGGT_GLOBAL_QB, WPEg = VGGT_GLOBAL_WPE;
-  constexpr int QBf = VGGT_G2F_QB, WPEf = VGGT_G2F_WPE;
-  const int BM = 64 * (p.g2f ? QBf : QBg);
+  const bool inplace = p.inplace;
+  const int qbn = p.g2f ? VGGT_G2F_QB : VGGT_GLOBAL_QB;
+  const int BM = 64 * qbn;
   if (p.g2f) {
     a.qtiles_per_frame = int((p.L + BM - 1) / BM);
     a.qtiles = a.qtiles_per_frame * p.frames;
@@ -894,38 +918,53 @@ hipError_t launch_attend(const vggt_attn_plan_s& p, const void* q, const void* k
   a.split_from = p.split_from;
   a.nsplit = p.nsplit;
   a.part = p.nsplit > 1 ? reinterpret_cast<float*>(base + p.layout.off_part) : nullptr;
+  a.kmax = p.prescale_q ? reinterpret_cast<const uint32_t*>(base + p.layout.off_kmax) : nullptr;
   const unsigned blocks = unsigned(p.split_from);
   const unsigned pblocks = unsigned(p.split_items * p.nsplit);
   const bool ob = p.out_dtype == VGGT_ATTN_BF16;
-  const bool pre = p.prescale_q;  // never set together with log_size
+  const bool pre = p.prescale_q;  // never set together with log_size, never in place
   const bool sz = p.log_size;
-#define VGGT_LAUNCH(QB_, WPE_, IP_)                                                                     \
-  do {                                                                                                 \
-    if (blocks > 0) {                                                                                  \
-      if (sz && ob) hipLaunchKernelGGL((attn_bf16_kernel<QB_, WPE_, true, false, true, false, IP_>), dim3(blocks), dim3(256), 0, stream, a);   \
-      else if (sz) hipLaunchKernelGGL((attn_bf16_kernel<QB_, WPE_, false, false, true, false, IP_>), dim3(blocks), dim3(256), 0, stream, a);  \
-      else if (ob && pre) hipLaunchKernelGGL((attn_bf16_kernel<QB_, WPE_, true, true, false, false, IP_>), dim3(blocks), dim3(256), 0, stream, a); \
-      else if (ob) hipLaunchKernelGGL((attn_bf16_kernel<QB_, WPE_, true, false, false, false, IP_>), dim3(blocks), dim3(256), 0, stream, a);  \
-      else if (pre) hipLaunchKernelGGL((attn_bf16_kernel<QB_, WPE_, false, true, false, false, IP_>), dim3(blocks), dim3(256), 0, stream, a); \
-      else hipLaunchKernelGGL((attn_bf16_kernel<QB_, WPE_, false, false, false, false, IP_>), dim3(blocks), dim3(256), 0, stream, a);        \
-    }                                                                                                  \
-    if (pblocks > 0) {                                                                                 \
-      if (ob) hipLaunchKernelGGL((attn_bf16_kernel<QB_, WPE_, true, false, false, true, IP_>), dim3(pblocks), dim3(256), 0, stream, a);       \
-      else hipLaunchKernelGGL((attn_bf16_kernel<QB_, WPE_, false, false, false, true, IP_>), dim3(pblocks), dim3(256), 0, stream, a);         \
-    }                                                                                                  \
-  } while (0)
-  // Every bf16 G2F plan reads K/V in place; the global forms read the packed copy.
-  if (p.g2f) VGGT_LAUNCH(QBf, WPEf, true);
-  else VGGT_LAUNCH(QBg, WPEg, false);
-#undef VGGT_LAUNCH
+  // One instantiation per (tiling, output type, score form, split, in-place) actually used.
+  auto go = [&](auto qb_, auto wpe_, auto ob_, auto pre_, auto sz_, auto ip_) {
+    constexpr int QB_ = decltype(qb_)::value, WPE_ = decltype(wpe_)::value;
+    constexpr bool OB = decltype(ob_)::value, PRE = decltype(pre_)::value, SZ = decltype(sz_)::value;
+    constexpr bool IP = decltype(ip_)::value;
+    if constexpr (!(PRE && (SZ || IP))) {
+      if (blocks > 0)
+        hipLaunchKernelGGL((attn_bf16_kernel<QB_, WPE_, OB, PRE, SZ, false, IP>), dim3(blocks), dim3(256), 0, stream, a);
+      if constexpr (!SZ) {
+        if (pblocks > 0)
+          hipLaunchKernelGGL((attn_bf16_kernel<QB_, WPE_, OB, PRE, false, true, IP>), dim3(pblocks), dim3(256), 0, stream, a);
+      }
+    }
+  };
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+  auto by_form = [&](auto qb_, auto wpe_, auto ip_) {
+    if (ob) {
+      if (sz) go(qb_, wpe_, T_{}, F_{}, T_{}, ip_);
+      else if (pre) go(qb_, wpe_, T_{}, T_{}, F_{}, ip_);
+      else go(qb_, wpe_, T_{}, F_{}, F_{}, ip_);
+    } else {
+      if (sz) go(qb_, wpe_, F_{}, F_{}, T_{}, ip_);
+      else if (pre) go(qb_, wpe_, F_{}, T_{}, F_{}, ip_);
+      else go(qb_, wpe_, F_{}, F_{}, F_{}, ip_);
+    }
+  };
+  using QBg = std::integral_constant<int, VGGT_GLOBAL_QB>;
+  using WPEg = std::integral_constant<int, VGGT_GLOBAL_WPE>;
+  using QBf = std::integral_constant<int, VGGT_G2F_QB>;
+  using WPEf = std::integral_constant<int, VGGT_G2F_WPE>;
+  // bf16 G2F plans read K/V in place, except in the f16 score form (packed f16 keys).
+  if (p.g2f && inplace) by_form(QBf{}, WPEf{}, T_{});
+  else if (p.g2f) by_form(QBf{}, WPEf{}, F_{});
+  else by_form(QBg{}, WPEg{}, F_{});
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.nsplit <= 1) return e;
-  // Split pieces run the exact-scale form: running maxima are raw scores.
-  const float m_scale = a.c_log2;
   const int64_t threads = p.split_items * BM * 16;
   const unsigned mblocks = unsigned((threads + 255) / 256);
-  if (ob) hipLaunchKernelGGL((merge_pieces_kernel<true>), dim3(mblocks), dim3(256), 0, stream, a, BM, m_scale);
-  else hipLaunchKernelGGL((merge_pieces_kernel<false>), dim3(mblocks), dim3(256), 0, stream, a, BM, m_scale);
+  if (ob) hipLaunchKernelGGL((merge_pieces_kernel<true>), dim3(mblocks), dim3(256), 0, stream, a, BM);
+  else hipLaunchKernelGGL((merge_pieces_kernel<false>), dim3(mblocks), dim3(256), 0, stream, a, BM);
   return hipGetLastError();
 }
 

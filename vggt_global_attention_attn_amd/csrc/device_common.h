@@ -23,6 +23,17 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return uint32_t(f32_to_bf16(lo)) | (uint32_t(f32_to_bf16(hi)) << 16);
 }
 
+// f16 score form: exponent e of the power-of-two key scale 2^-e of one head, from the bf16 bits
+// of the largest |k| among its packed keys.  e puts that maximum in [128, 256), so every scaled
+// key lies in f16's range and is exact there down to 2^-22 of the maximum; e is clamped to
+// [-120, 120] so that 2^e and 2^-e are normal float32 values.
+__device__ __forceinline__ int key_scale_exp(uint32_t kmax_bits) {
+  if (kmax_bits == 0) return 0;
+  const float km = __uint_as_float(kmax_bits << 16);
+  const int e = __builtin_amdgcn_frexp_expf(km) - 8;  // km = m * 2^x, m in [0.5, 1): floor(log2 km) = x - 1
+  return e < -120 ? -120 : (e > 120 ? 120 : e);
+}
+
 // t[i] for a run-time i, written as a chain of selects over compile-time indices (a fold
 // expression, so every access has a constant index before any loop pass runs): indexing an
 // array of the kernel-argument struct with a run-time value would make the compiler copy the

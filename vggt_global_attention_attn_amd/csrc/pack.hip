@@ -161,6 +161,7 @@ struct PackArgs {
   void* vpack;        // bf16: [H][rows/64][64][64] key-minor; fp32: [H][rows][64]
   int32_t* index;     // [|S|] or nullptr
   int32_t* dcount;    // [N]
+  uint32_t* kmax;     // [H] bf16 bits of the largest packed |k| (f16 score form), else nullptr
   int64_t T;
   int64_t rows_per_head;
   int64_t nS;
@@ -204,6 +205,7 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a) {
   E* VP = static_cast<E*>(a.vpack) + (size_t(h) * a.rows_per_head + size_t(tile) * kTile) * kHeadDim;
   // V rows of the tile, padded to 68 halves per row for conflict-light column reads.
   __shared__ uint16_t vt[TRANSPOSE_V ? kTile : 1][68];
+  uint32_t kabs = 0;  // largest |k| seen by this thread, as bf16 bits (bf16 inputs)
   for (int e = tid; e < CHUNKS; e += 256) {
     const int row = e / CPR, ch = e % CPR;
     const int64_t prow = int64_t(tile) * kTile + row;
@@ -220,6 +222,11 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a) {
     }
     *reinterpret_cast<uint4*>(KP + size_t(row) * kHeadDim + ch * CH) = kv;
     if constexpr (TRANSPOSE_V) {
+      const uint32_t w[4] = {kv.x, kv.y, kv.z, kv.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) kabs = max(kabs, max(w[i] & 0x7fffu, (w[i] >> 16) & 0x7fffu));
+    }
+    if constexpr (TRANSPOSE_V) {
       uint2* dst = reinterpret_cast<uint2*>(&vt[row][ch * CH]);
       dst[0] = make_uint2(vv.x, vv.y);
       dst[1] = make_uint2(vv.z, vv.w);
@@ -230,6 +237,13 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a) {
   if (a.dcount && h == 0 && tile == 0) {
     for (int f = tid; f < a.frames; f += 256)
       a.dcount[f] = frame_dropped(a.g, f);
+  }
+  if constexpr (TRANSPOSE_V) {
+    if (a.kmax) {  // (non-negative bf16 bits order like the values)
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) kabs = max(kabs, uint32_t(__shfl_xor(int(kabs), off)));
+      if ((tid & 63) == 0 && kabs > 0) atomicMax(&a.kmax[h], kabs);
+    }
   }
   if constexpr (TRANSPOSE_V) {
     __syncthreads();
@@ -257,6 +271,35 @@ __global__ __launch_bounds__(256) void index_kernel(PackArgs a) {
   if (a.index)
     for (int64_t i = first; i < a.nS; i += stride) a.index[i] = int32_t(token_of_kept_index(a.g, i));
   for (int64_t f = first; f < a.frames; f += stride) a.dcount[f] = frame_dropped(a.g, int(f));
+}
+
+// f16 score form, before the pack: the per-head maxima start at zero.
+__global__ __launch_bounds__(256) void kmax_clear_kernel(uint32_t* kmax, int heads) {
+  const int h = blockIdx.x * 256 + threadIdx.x;
+  if (h < heads) kmax[h] = 0;
+}
+
+// f16 score form, after the pack: packed bf16 keys of head h -> f16(k * 2^-e_h) in place (an
+// exact conversion for |k| above 2^-22 of the head's maximum, which sits in [128, 256)).  One
+// thread per 16-byte chunk of 8 values.
+__global__ __launch_bounds__(256) void kpack_f16_kernel(uint16_t* kpack, const uint32_t* kmax,
+                                                        int64_t chunks_per_head, int64_t chunks) {
+  const int64_t stride = int64_t(gridDim.x) * 256;
+  for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < chunks; i += stride) {
+    const int h = int(i / chunks_per_head);
+    const float scale = __builtin_amdgcn_ldexpf(1.f, -key_scale_exp(kmax[h]));
+    uint4* p = reinterpret_cast<uint4*>(kpack) + i;
+    const uint4 raw = *p;
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const _Float16 lo = (_Float16)(__uint_as_float(w[j] << 16) * scale);
+      const _Float16 hi = (_Float16)(__uint_as_float(w[j] & 0xffff0000u) * scale);
+      o[j] = uint32_t(__builtin_bit_cast(uint16_t, lo)) | (uint32_t(__builtin_bit_cast(uint16_t, hi)) << 16);
+    }
+    *p = make_uint4(o[0], o[1], o[2], o[3]);
+  }
 }
 
 struct SizeBiasArgs {
@@ -352,17 +395,31 @@ hipError_t launch_pack(const vggt_attn_plan_s& p, const void* k, const void* v, 
   a.segment_rows = int(p.segment_rows);
   a.frames = p.frames;
   a.g = p.geom;
+  a.kmax = p.prescale_q ? reinterpret_cast<uint32_t*>(base + p.layout.off_kmax) : nullptr;
   if (p.inplace) {
     const int64_t work = std::max<int64_t>(a.index ? p.nS : 0, p.frames);
     const unsigned blocks = unsigned(std::min<int64_t>((work + 255) / 256, 4096));
     hipLaunchKernelGGL(index_kernel, dim3(blocks), dim3(256), 0, stream, a);
     return hipGetLastError();
   }
+  if (a.kmax) {
+    hipLaunchKernelGGL(kmax_clear_kernel, dim3(unsigned((p.heads + 255) / 256)), dim3(256), 0, stream, a.kmax, p.heads);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   const dim3 grid(unsigned(p.rows_per_head / kTile), unsigned(p.heads));
   if (p.in_dtype == VGGT_ATTN_BF16)
     hipLaunchKernelGGL((pack_kernel<uint16_t, true>), grid, dim3(256), 0, stream, a);
   else
     hipLaunchKernelGGL((pack_kernel<float, false>), grid, dim3(256), 0, stream, a);
+  if (!a.kmax) return hipGetLastError();
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t per_head = p.rows_per_head * kHeadDim / 8;
+  const int64_t chunks = per_head * p.heads;
+  const unsigned blocks = unsigned(std::min<int64_t>((chunks + 255) / 256, 8192));
+  hipLaunchKernelGGL(kpack_f16_kernel, dim3(blocks), dim3(256), 0, stream, static_cast<uint16_t*>(a.kpack),
+                     static_cast<const uint32_t*>(a.kmax), per_head, chunks);
   return hipGetLastError();
 }
 

@@ -90,7 +90,7 @@ int build_plan(vggt_attn_plan_s* p, int frames, int grid_h, int grid_w, int n_sp
   p->mean_global = (flags & VGGT_ATTN_MEAN_GLOBAL) && p->mean;
   p->mean_count = flags & VGGT_ATTN_MEAN_COUNT;
   p->log_size = flags & VGGT_ATTN_LOG_SIZE;
-  p->prescale_q = (flags & VGGT_ATTN_PRESCALE_Q) && !p->log_size;
+  p->prescale_q = (flags & VGGT_ATTN_PRESCALE_Q) && !p->log_size && in_dtype == VGGT_ATTN_BF16;
   p->phase = (flags & VGGT_ATTN_PHASE_SHIFT) && p->subsampled;
   p->s_h = s_h; p->s_w = s_w;
   p->L = int(L); p->P = int(P); p->T = T;
@@ -173,7 +173,7 @@ int build_plan(vggt_attn_plan_s* p, int frames, int grid_h, int grid_w, int n_sp
     return fail(err, VGGT_ATTN_EINVAL, "packed rows per head %lld exceed %lld", p->rows_per_head, kMaxPackedRows);
 
   // bf16 work items and the split of a sparse last round (float32 inputs: one item per 64 rows,
-  // never split; nor are the PRESCALE_Q and LOG_SIZE forms).
+  // never split; nor is the LOG_SIZE form).
   const int qb = g2f ? VGGT_G2F_QB : VGGT_GLOBAL_QB;
   const int wpe = g2f ? VGGT_G2F_WPE : VGGT_GLOBAL_WPE;
   p->block_rows = in_dtype == VGGT_ATTN_BF16 ? 64 * qb : 64;
@@ -182,7 +182,7 @@ int build_plan(vggt_attn_plan_s* p, int frames, int grid_h, int grid_w, int n_sp
   p->split_from = p->work_items;
   p->split_items = 0;
   p->nsplit = 1;
-  if (in_dtype == VGGT_ATTN_BF16 && !p->prescale_q && !p->log_size) {
+  if (in_dtype == VGGT_ATTN_BF16 && !p->log_size) {
     const int64_t slots = int64_t(kComputeUnits) * wpe;
     const int64_t tail = p->work_items % slots;
     const int64_t nkt = p->segment_rows / kTile;
@@ -194,7 +194,8 @@ int build_plan(vggt_attn_plan_s* p, int frames, int grid_h, int grid_w, int n_sp
     }
   }
 
-  p->inplace = in_dtype == VGGT_ATTN_BF16 && g2f;
+  // bf16 G2F reads K and V in place, unless the f16 score form needs K converted and packed.
+  p->inplace = in_dtype == VGGT_ATTN_BF16 && g2f && !p->prescale_q;
   p->elem_bytes = in_dtype == VGGT_ATTN_BF16 ? 2 : 4;
   vggt_attn_layout_t& lay = p->layout;
   lay.segments = p->segments;
@@ -210,6 +211,7 @@ int build_plan(vggt_attn_plan_s* p, int frames, int grid_h, int grid_w, int n_sp
   lay.off_logsize = off; off = align256(off + (p->log_size ? T * 4 : 0));
   lay.off_part = off;   off = align256(off + p->split_items * p->nsplit * p->block_rows * kPartRow * 4 * (p->nsplit > 1));
   lay.split_pieces = p->nsplit > 1 ? p->nsplit : 0;
+  lay.off_kmax = off;   off = align256(off + (p->prescale_q ? int64_t(heads) * 4 : 0));
   const int64_t packed = p->inplace ? 0 : int64_t(heads) * p->rows_per_head * head_dim * int64_t(p->elem_bytes);
   lay.off_kpack = off;  off = align256(off + packed);
   lay.off_vpack = off;  off = align256(off + packed);

@@ -88,7 +88,8 @@ struct vggt_attn_plan_s {
   int64_t segments, segment_rows, keys_per_segment, n_plain, rows_per_head;
   // bf16 G2F plans read K and V where they lie (the keys of a frame are its tokens, in order):
   // no packed copy; the pack stage writes only the per-frame counts.  (Dense plans could do the
-  // same, but there the transposed V reads cost more attention time than the O(T) pack.)
+  // same, but there the transposed V reads cost more attention time than the O(T) pack.)  The
+  // f16 score form (prescale_q) packs G2F keys too: they are converted to f16.
   bool inplace;
   // bf16 attention work split: work items (query tile x head) below split_from run whole; the
   // split_items after them run as nsplit key-range pieces each, merged by a second kernel.
