@@ -58,19 +58,25 @@ WORKLOADS = {
     "g2m-32f": (dict(frames=32, grid_h=37, grid_w=37, heads=16, g2m=True),
                 "32 frames x 1374 tokens, 16 heads, d=64, bf16 in / fp32 out, Global-to-Mean (one mean K/V token)"),
 }
+# The f16 score form (PRESCALE_Q) of a workload: packed keys f16(k * 2^-e_h), Q * tau * log2(e) *
+# 2^e_h rounded to f16 once, QK^T on the f16 matrix cores (same peak as bf16), PV on bf16.
+for _n in ("sga6-800f", "dense-32f", "g2f-200f", "sga9-200f"):
+    _d, _t = WORKLOADS[_n]
+    WORKLOADS[_n + "-f16"] = (dict(_d, prescale_q=True), _t + "; f16 score form (Q*tau*log2e rounded to f16 once)")
 
 # Reported beside the headline workload (same run, fewer steps).  Each group shares one set of
 # tensors: the 200-frame group runs G2F and then SGA sigma 9 (plain, then on the phase-shifted
 # grid with one global mean), the early/middle layer split.
 EXTRA_GROUPS = [
     ("tiny-fp32", [dict(frames=4, grid_h=8, grid_w=8, heads=2, sigma=4, diag=True, mean=True)], "fp32"),
-    ("dense+g2m-32f", [WORKLOADS["dense-32f"][0], WORKLOADS["g2m-32f"][0]], "bf16"),
+    ("dense+g2m-32f", [WORKLOADS["dense-32f"][0], WORKLOADS["dense-32f-f16"][0], WORKLOADS["g2m-32f"][0]], "bf16"),
     ("sga4-100f", [WORKLOADS["sga4-100f"][0]], "bf16"),
-    ("g2f+sga9-200f", [WORKLOADS["g2f-200f"][0], WORKLOADS["sga9-200f"][0], WORKLOADS["sga9-200f-phase-global"][0]],
-     "bf16"),
+    ("g2f+sga9-200f", [WORKLOADS["g2f-200f"][0], WORKLOADS["g2f-200f-f16"][0], WORKLOADS["sga9-200f"][0],
+                       WORKLOADS["sga9-200f-f16"][0], WORKLOADS["sga9-200f-phase-global"][0]], "bf16"),
 ]
 # Run on the headline workload's own tensors (same geometry), before they are released.
-SAME_TENSOR_EXTRAS = {"sga6-800f": ["sga6-800f-phase", "sga6-800f-sized"], "sga6-800f-phase": ["sga6-800f"]}
+SAME_TENSOR_EXTRAS = {"sga6-800f": ["sga6-800f-f16", "sga6-800f-phase", "sga6-800f-sized"],
+                      "sga6-800f-phase": ["sga6-800f"], "sga6-800f-f16": ["sga6-800f"]}
 
 
 def form_name(d) -> str:
@@ -85,6 +91,8 @@ def form_name(d) -> str:
         name += "-globalmean"
     if d.get("log_size"):
         name += "-sized"
+    if d.get("prescale_q"):
+        name += "-f16"
     return name
 
 
@@ -375,11 +383,19 @@ def main() -> int:
         del qd, kd, vd
         torch.cuda.empty_cache()
         result["other_workloads"] = same + extra_workloads(dev, steps=3)
+        # The same attention kernel in the f16 score form on the headline tensors (opt-in flag).
+        for e in same:
+            if e["name"] == args.workload + "-f16":
+                a = e["attention"][0]
+                result["roofline_f16_score_form"] = {
+                    "bound": "mfma", "kernel": "attn_bf16_kernel (PRESCALE_Q)", "achieved": a["tflops"],
+                    "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": a["frac_bf16_peak"],
+                    "note": "QK^T on f16 matrix cores (same dense peak as bf16), PV on bf16"}
 
     if not args.no_cpu_baseline:
         import oracle
         from oracle import Desc
-        odesc = Desc(**desc)
+        odesc = Desc(**{k: v for k, v in desc.items() if k != "prescale_q"})
         cores = host_threads()
         log(f"oracle on {rows.size} rows x {H} heads with {cores} threads")
         c0 = time.perf_counter()

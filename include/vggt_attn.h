@@ -183,14 +183,15 @@ int vggt_attn_forward(const vggt_attn_plan_t* plan, const void* q, const void* k
  * biases, and the packed keys and values: rows [0,|S|) are exact copies of K/V rows of S, rows
  * [|S|, |S|+M) the means, padding rows zero.  Under sigma = 1 it packs every token; under G2F
  * float32 plans pack every token frame by frame, while bf16 plans write |D_f| only, since their
- * attention stage reads k and v in place.  |D_f| is L for every frame under G2M.  Reads k and
- * v only. */
+ * attention stage reads k and v in place (with PRESCALE_Q they pack frame by frame too).  With
+ * PRESCALE_Q the packed keys are then converted to f16 as the flag describes, and off_kmax holds
+ * each head's largest packed |k|.  |D_f| is L for every frame under G2M.  Reads k and v only. */
 int vggt_attn_pack(const vggt_attn_plan_t* plan, const void* k, const void* v, void* workspace,
                    size_t workspace_bytes, void* stream);
 
 /* Attention stage on a workspace already filled by vggt_attn_pack for the same plan and the
  * same k, v (k and v are read again for the diagonal term, and for every key by bf16 G2F
- * plans, which keep no packed copy).  Writes every element of out.  It
+ * plans without PRESCALE_Q, which keep no packed copy).  Writes every element of out.  It
  * uses the workspace's off_part area as scratch (the partial softmax states of a split last
  * round of work-groups, see vggt_attn_layout_t) and leaves the packed parts unchanged, so it
  * may be called again on the same workspace. */
