@@ -81,7 +81,7 @@ SAME_TENSOR_EXTRAS = {"sga6-800f": ["sga6-800f-f16", "sga6-800f-phase", "sga6-80
 
 def form_name(d) -> str:
     if d.get("g2f"):
-        return "g2f"
+        return "g2f-f16" if d.get("prescale_q") else "g2f"
     if d.get("g2m"):
         return "g2m"
     name = f"sigma{d.get('sigma', 1)}"

@@ -240,9 +240,18 @@ __global__ __launch_bounds__(256) void pack_kernel(PackArgs a) {
   }
   if constexpr (TRANSPOSE_V) {
     if (a.kmax) {  // (non-negative bf16 bits order like the values)
+      // One atomic per work-group at most, and none once the head's maximum is at least this
+      // tile's (the maximum only grows, so a stale read can only cause a redundant atomic).
+      __shared__ uint32_t wmax[4];
 #pragma unroll
       for (int off = 32; off > 0; off >>= 1) kabs = max(kabs, uint32_t(__shfl_xor(int(kabs), off)));
-      if ((tid & 63) == 0 && kabs > 0) atomicMax(&a.kmax[h], kabs);
+      if ((tid & 63) == 0) wmax[tid >> 6] = kabs;
+      __syncthreads();
+      if (tid == 0) {
+        kabs = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
+        if (kabs > __hip_atomic_load(&a.kmax[h], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+          atomicMax(&a.kmax[h], kabs);
+      }
     }
   }
   if constexpr (TRANSPOSE_V) {
