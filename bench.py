@@ -257,7 +257,7 @@ def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
-    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="sga6-800f", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=1024, help="query rows in the oracle sample")
@@ -336,6 +336,8 @@ def main() -> int:
     wall = time.perf_counter() - w0
     t_gather = sum(e0.elapsed_time(e1) for e0, e1, _ in ev) / len(ev) * 1e-3
     t_attn = sum(e1.elapsed_time(e2) for _, e1, e2 in ev) / len(ev) * 1e-3
+    fwd_ms = sorted(e0.elapsed_time(e2) for e0, _, e2 in ev)
+    t_fwd_median = fwd_ms[len(fwd_ms) // 2] * 1e-3
     step_s = wall / args.steps
     log(f"timed {args.steps} steps: {step_s * 1e3:.3f} ms/step (gather {t_gather * 1e3:.3f} ms, attention {t_attn * 1e3:.3f} ms)")
 
@@ -368,6 +370,7 @@ def main() -> int:
         "pct_bf16_peak": 100.0 * flops / step_s / 1e12 / MFMA_BF16_PEAK_TFLOPS,
         "t_gather_ms": t_gather * 1e3,
         "t_attn_ms": t_attn * 1e3,
+        "t_fwd_median_ms": t_fwd_median * 1e3,
         "gather": {"bytes": gbytes, "GB/s": gbytes / t_gather / 1e9, "frac_hbm_peak": gbytes / t_gather / 1e9 / HBM_PEAK_GBS},
         "roofline": {"bound": "mfma", "kernel": "attn_bf16_kernel", "achieved": achieved,
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
@@ -403,8 +406,10 @@ def main() -> int:
         c_s = time.perf_counter() - c0
         got = out_rows
         diff = got - ref
+        oflops = flops * rows.size / T  # the same formula restricted to the sampled rows
         result["cpu_baseline"] = {
             "value": rows.size / c_s, "unit": "queries/s", "cores": cores, "kind": "oracle",
+            "gflops": oflops / c_s / 1e9,
             "sample": f"{rows.size} seeded query rows (all {H} heads) of the same workload, float64 NumPy, "
                       f"{c_s:.1f} s including its own index-set and mean computation",
             "seconds": c_s,

@@ -225,8 +225,8 @@ void attn_bf16_kernel(AttnArgs a) {
   // from it.  Before tile 0 the slot holds the diagonal term's logit (raw or log2 units).
   float m_run[QB], l_run[QB];
   f32x4_t o[QB][4];
-  // Two ways to reach log2 units.  Exact (default): Q is used as given, scores and the running
-  // max are in units of q.k, and the exp2 argument is multiplied by c = tau*log2(e).
+  // Two ways to reach log2 units.  Exact (default): Q is used as given, scores are in units of
+  // q.k, and the exp2 argument is c s plus the offset, c = tau*log2(e).
   // f16 score form (PRESCALE_Q plan flag): the packed keys of head h are f16(k * 2^-e_h) and Q
   // is scaled by c * 2^e_h once and rounded to f16, so that the f16 matrix cores deliver scores
   // in log2 units and the running max enters their accumulator: no multiply per score.  The
