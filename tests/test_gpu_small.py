@@ -1,10 +1,12 @@
 """GPU parity at sizes the oracle finishes in seconds: several key and query tiles, ragged
 tails, every form (dense, SGA sigma 2/4/6/9, enhanced SGA with UNIT and COUNT means, pi^3
 without a dense frame, the phase-shifted grid, the global mean scope, G2F, G2M), both output
-types, plus the bit-exact index set and packed rows, V = 1, determinism, a NaN-poisoned
-workspace, the tied-Q/K stress input, the collapse identity (identical dropped rows under COUNT
-means equal dense attention), G2F's in-place reads stopping at the tensors' end, and the C ABI's
-error codes.  Every call goes through the C ABI of libvggt_attn.so."""
+types, the exact and the f16 score form, plus the bit-exact index set and packed rows (and the
+f16 packed keys), V = 1, determinism, a NaN-poisoned workspace, the rising-logit, spike and
+tied-Q/K stress inputs, the collapse identity (identical dropped rows under COUNT means equal
+dense attention), G2F's in-place reads stopping at the tensors' end, degenerate shapes (one
+token, one frame, nothing dropped, no specials), and the C ABI's error codes.  Every call goes
+through the C ABI of libvggt_attn.so."""
 import ctypes
 import zlib
 
@@ -452,3 +454,29 @@ def test_g2f_reads_stop_at_tensor_end(lib):
     torch.cuda.synchronize()
     got = out.float().cpu().numpy()
     assert_close(got, oracle.attention(q, k, v, desc), fp32=False, label="g2f-poisoned-tail")
+
+
+EDGE = [
+    (Desc(1, 1, 1, 1, n_special=0, sigma=1), "one-token"),
+    (Desc(1, 1, 1, 2, n_special=0, g2f=True), "one-token-g2f"),
+    (Desc(1, 4, 5, 2, sigma=6, diag=True, mean=True), "one-frame-sga6"),      # frame 0 dense: every key kept
+    (Desc(2, 1, 1, 1, n_special=0, sigma=4, diag=True, mean=True), "one-patch-frames"),  # nothing dropped
+    (Desc(3, 9, 8, 1, n_special=0, sigma=9, diag=True, mean=True, mean_count=True), "no-specials-sga9"),
+    (Desc(2, 2, 65, 1, n_special=0, sigma=2, diag=True, mean=True, ref_dense=False), "wide-grid-pi3"),
+    (Desc(3, 13, 11, 1, n_special=7, sigma=6, diag=True, mean=True, phase_shift=True), "seven-specials-phase"),
+]
+
+
+@pytest.mark.parametrize("desc,label", EDGE, ids=[c[1] for c in EDGE])
+@pytest.mark.parametrize("prescale_q", [False, True], ids=["exact", "f16"])
+def test_edge_shapes(lib, desc, label, prescale_q):
+    """Degenerate geometries: a single token (softmax over one key: out = v), a single frame
+    (everything dense), one-patch frames (no dropped patch, so no diagonal or mean term), no
+    special tokens, a grid one row high, more specials than usual; exact and f16 score forms."""
+    q, k, v = inputs_for(desc, "bf16", seed=31)
+    _, got, _, _ = run(lib, desc, q, k, v, prescale_q=prescale_q)
+    ref = oracle.attention(q, k, v, desc, workers=4)
+    assert_close(got, ref, fp32=False, label=f"{label}/{'f16' if prescale_q else 'exact'}")
+    if desc.T == 1:
+        from synth import bf16_bits_to_f32
+        assert np.array_equal(got, bf16_bits_to_f32(v).astype(np.float32))  # one key: weight exactly 1
