@@ -376,6 +376,8 @@ def main() -> int:
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
                      "traffic": traffic, "algorithmic_flops_per_launch": flops},
         "device": torch.cuda.get_device_name(dev),
+        "compute_units": torch.cuda.get_device_properties(dev).multi_processor_count,
+        "hip_version": torch.version.hip,
     }
 
     if not args.no_extra:
