@@ -10,7 +10,8 @@
 // the sampling grid, which sets |D_f| and so the bias of each frame's mean key).
 //
 // attn_bf16_kernel: flash-style forward on the bf16 matrix cores (v_mfma_f32_16x16x32_bf16,
-// float32 accumulation).  A work-group of 4 waves owns BM = 4*16*QB query rows of one head and
+// float32 accumulation; in the opt-in f16 score form Q K^T runs on v_mfma_f32_16x16x32_f16 with
+// the softmax scale folded into Q).  A work-group of 4 waves owns BM = 4*16*QB query rows of one head and
 // streams the key segment -- the packed workspace, or under G2F the frame's own rows of K and
 // V read in place -- in 64-key tiles through LDS filled by direct global->LDS buffer loads.
 // Work items are numbered XCD by XCD, so that neighbouring items share an L2.  Scores are
