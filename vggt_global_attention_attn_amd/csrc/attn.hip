@@ -925,6 +925,7 @@ hipError_t launch_attend(const vggt_attn_plan_s& p, const void* q, const void* k
   const bool ob = p.out_dtype == VGGT_ATTN_BF16;
   const bool pre = p.prescale_q;  // never set together with log_size, never in place
   const bool sz = p.log_size;
+  if (pre && (sz || inplace)) return hipErrorInvalidValue;  // (the plan never combines them)
   // One instantiation per (tiling, output type, score form, split, in-place) actually used.
   auto go = [&](auto qb_, auto wpe_, auto ob_, auto pre_, auto sz_, auto ip_) {
     constexpr int QB_ = decltype(qb_)::value, WPE_ = decltype(wpe_)::value;
