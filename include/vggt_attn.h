@@ -75,9 +75,9 @@ enum {
                                      the f16 matrix cores.  The pack stage converts the packed keys
                                      of head h to f16 after scaling them by 2^-e_h, where e_h puts
                                      the head's largest packed |k| in [128, 256) (exact for every
-                                     |k| above 2^-22 of that maximum); the attention stage rounds
+                                     |k| above 2^-21 of that maximum); the attention stage rounds
                                      Q * tau * log2(e) * 2^e_h to f16 once.  Saves one multiply
-                                     per score (about 8% faster); each logit term then carries a
+                                     per score (5-6% faster at 800 frames); each logit term then carries a
                                      relative error of up to 2^-11.  Without the flag Q and K are
                                      used exactly as given and the scale is applied in float32.
                                      G2F plans with the flag pack K and V like the global forms.

@@ -25,7 +25,7 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 
 // f16 score form: exponent e of the power-of-two key scale 2^-e of one head, from the bf16 bits
 // of the largest |k| among its packed keys.  e puts that maximum in [128, 256), so every scaled
-// key lies in f16's range and is exact there down to 2^-22 of the maximum; e is clamped to
+// key lies in f16's range and is exact there down to 2^-21 of the maximum; e is clamped to
 // [-120, 120] so that 2^e and 2^-e are normal float32 values.
 __device__ __forceinline__ int key_scale_exp(uint32_t kmax_bits) {
   if (kmax_bits == 0) return 0;

@@ -289,7 +289,7 @@ __global__ __launch_bounds__(256) void kmax_clear_kernel(uint32_t* kmax, int hea
 }
 
 // f16 score form, after the pack: packed bf16 keys of head h -> f16(k * 2^-e_h) in place (an
-// exact conversion for |k| above 2^-22 of the head's maximum, which sits in [128, 256)).  One
+// exact conversion for |k| above 2^-21 of the head's maximum, which sits in [128, 256)).  One
 // thread per 16-byte chunk of 8 values.
 __global__ __launch_bounds__(256) void kpack_f16_kernel(uint16_t* kpack, const uint32_t* kmax,
                                                         int64_t chunks_per_head, int64_t chunks) {
