@@ -114,6 +114,8 @@ class Sized:
 KERNEL_SOURCES = ("vggt_global_attention_attn_amd/csrc/attn.hip", "vggt_global_attention_attn_amd/csrc/device_common.h",
                   "vggt_global_attention_attn_amd/csrc/plan.h")
 TRAFFIC_FILE = "profiles/attn_{workload}_hbm_traffic.txt"
+CLOCK_FILE = "profiles/attn_{workload}_clock.txt"
+MFMA_BF16_FLOP_PER_CLK_CU = 4096  # 16x16x32 bf16 MFMA: 16384 flop per 16 cycles per SIMD, 4 SIMDs per CU
 
 
 def log(msg: str) -> None:
@@ -134,10 +136,10 @@ def kernel_source_hash() -> str:
     return h.hexdigest()
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per attention launch from the committed rocprofv3 PMC summary, if it was taken
-    on the current kernel source; else None."""
-    path = os.path.join(ROOT, TRAFFIC_FILE.format(workload=workload))
+def profile_record(template: str, workload: str):
+    """The JSON record of a committed rocprofv3 summary, if it was taken on the current kernel
+    source; else None."""
+    path = os.path.join(ROOT, template.format(workload=workload))
     if not os.path.exists(path):
         return None
     rec = None
@@ -148,7 +150,33 @@ def measured_traffic(workload: str):
                 rec = json.loads(line)
     if not rec or rec.get("source_sha256") != kernel_source_hash():
         return None
-    return rec.get("hbm_bytes_per_launch")
+    return rec
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per attention launch from the committed PMC summary (FETCH_SIZE, WRITE_SIZE)."""
+    rec = profile_record(TRAFFIC_FILE, workload)
+    return rec.get("hbm_bytes_per_launch") if rec else None
+
+
+def measured_clock(workload: str):
+    """Sustained shader clock (GHz) of the attention kernel from the committed GRBM_GUI_ACTIVE
+    summary of the same workload."""
+    rec = profile_record(CLOCK_FILE, workload)
+    return rec.get("gfx_clock_ghz") if rec else None
+
+
+def clock_fields(flops: float, workload: str, cus: int) -> dict:
+    """The bf16 matrix-core peak at the clock the kernel sustains, and the fraction of it reached,
+    both from the committed GRBM_GUI_ACTIVE run (its own clock and kernel duration: the clock
+    differs from box to box, so this run's time is not divided by another run's clock)."""
+    rec = profile_record(CLOCK_FILE, workload)
+    if rec is None:
+        return {"clock_ghz": None, "peak_at_clock": None, "frac_at_clock": None}
+    ghz = rec["gfx_clock_ghz"]
+    peak = cus * MFMA_BF16_FLOP_PER_CLK_CU * ghz * 1e9 / 1e12
+    return {"clock_ghz": ghz, "peak_at_clock": peak, "frac_at_clock": flops / rec["duration_s"] / 1e12 / peak,
+            "clock_source": CLOCK_FILE.format(workload=workload)}
 
 
 def gather_bytes(desc, c) -> int:
@@ -374,7 +402,8 @@ def main() -> int:
         "gather": {"bytes": gbytes, "GB/s": gbytes / t_gather / 1e9, "frac_hbm_peak": gbytes / t_gather / 1e9 / HBM_PEAK_GBS},
         "roofline": {"bound": "mfma", "kernel": "attn_bf16_kernel", "achieved": achieved,
                      "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": achieved / MFMA_BF16_PEAK_TFLOPS,
-                     "traffic": traffic, "algorithmic_flops_per_launch": flops},
+                     "traffic": traffic, "algorithmic_flops_per_launch": flops,
+                     **clock_fields(flops, args.workload, torch.cuda.get_device_properties(dev).multi_processor_count)},
         "device": torch.cuda.get_device_name(dev),
         "compute_units": torch.cuda.get_device_properties(dev).multi_processor_count,
         "hip_version": torch.version.hip,
@@ -395,6 +424,8 @@ def main() -> int:
                 result["roofline_f16_score_form"] = {
                     "bound": "mfma", "kernel": "attn_bf16_kernel (PRESCALE_Q)", "achieved": a["tflops"],
                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": a["frac_bf16_peak"],
+                    "traffic": measured_traffic(e["name"]),
+                    **clock_fields(flops, e["name"], torch.cuda.get_device_properties(dev).multi_processor_count),
                     "note": "QK^T on f16 matrix cores (same dense peak as bf16), PV on bf16"}
 
     if not args.no_cpu_baseline:
