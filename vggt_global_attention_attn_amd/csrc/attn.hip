@@ -427,7 +427,8 @@ void attn_bf16_kernel(AttnArgs a) {
     if (next) scores_qb(kf, bb, qb, s_next, m_run[qb]);
     const float l_prev = l_run[qb];
     const uint32_t bits = probs_qb(qb, s_cur, pf);
-    if (__builtin_amdgcn_ballot_w64((bits & 0x40004000u) != 0) != 0) {
+    // (expected false: the rescale is laid out of line, so the common path runs straight on)
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64((bits & 0x40004000u) != 0) != 0, 0)) {
       asm volatile("; rare rescale" ::);  // keeps this branch from being speculated into every tile
       // Exact mode: scores are absolute (q.k); the offset drops to -(c mx + w) for the row max
       // mx.  f16 score form: scores are relative to m + w (log2 units), so the offset drops by
