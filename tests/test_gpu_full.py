@@ -41,6 +41,7 @@ FULL = [
 ]
 
 _cache = {}
+_refs = {}  # oracle rows of the last workload, shared by its exact and f16 score-form cases
 
 
 def device_inputs(desc):
@@ -85,8 +86,12 @@ def test_full_size_sampled_rows(name, desc):
     rows = sample_rows(desc.frames, desc.grid_h, desc.grid_w, desc.n_special, count=4096, seed=1)
     got = out[:, torch.from_numpy(rows).cuda()].double().cpu().numpy()
     del out, ws
-    print(f"[full] {name}: oracle on {rows.size} rows", flush=True)
-    ref = oracle.attention(q, k, v, desc, rows=rows, workers=host_threads(), log_g=log_g)
+    base = name[:-len("-f16")] if name.endswith("-f16") else name
+    if base not in _refs:
+        print(f"[full] {name}: oracle on {rows.size} rows", flush=True)
+        _refs.clear()
+        _refs[base] = oracle.attention(q, k, v, desc, rows=rows, workers=host_threads(), log_g=log_g)
+    ref = _refs[base]
     print(f"[full] {name}: max-abs %.3e rel-L2 %.3e" % errors(got, ref), flush=True)
     assert_close(got, ref, fp32=False, label=name)
 
