@@ -5,7 +5,8 @@ types, the exact and the f16 score form, plus the bit-exact index set and packed
 f16 packed keys), V = 1, determinism, a NaN-poisoned workspace, the rising-logit, spike and
 tied-Q/K stress inputs, the collapse identity (identical dropped rows under COUNT means equal
 dense attention), G2F's in-place reads stopping at the tensors' end, degenerate shapes (one
-token, one frame, nothing dropped, no specials), and the C ABI's error codes.  Every call goes
+token, one frame, nothing dropped, no specials), 160 seeded random configurations, and the C
+ABI's error codes.  Every call goes
 through the C ABI of libvggt_attn.so."""
 import ctypes
 import zlib
@@ -480,3 +481,48 @@ def test_edge_shapes(lib, desc, label, prescale_q):
     if desc.T == 1:
         from synth import bf16_bits_to_f32
         assert np.array_equal(got, bf16_bits_to_f32(v).astype(np.float32))  # one key: weight exactly 1
+
+
+def _random_desc(rng):
+    """A seeded random valid descriptor: geometry, form and options."""
+    frames = int(rng.integers(1, 10))
+    gh, gw = int(rng.integers(1, 21)), int(rng.integers(1, 21))
+    ns = int(rng.integers(0, 8))
+    heads = int(rng.integers(1, 4))
+    form = rng.choice(["dense", "sga", "g2f", "g2m"], p=[0.15, 0.65, 0.12, 0.08])
+    if form == "g2f":
+        return Desc(frames, gh, gw, heads, n_special=ns, g2f=True, log_size=bool(rng.random() < 0.3))
+    if form == "g2m":
+        return Desc(frames, gh, gw, heads, n_special=ns, g2m=True)
+    sigma = 1 if form == "dense" else int(rng.choice([2, 4, 6, 9]))
+    log_size = bool(rng.random() < 0.2)
+    mean = (not log_size) and bool(rng.random() < 0.7)
+    return Desc(frames, gh, gw, heads, n_special=ns, sigma=sigma, ref_dense=bool(rng.random() < 0.7),
+                diag=bool(rng.random() < 0.7), mean=mean, mean_count=mean and bool(rng.random() < 0.5),
+                phase_shift=bool(rng.random() < 0.4), mean_global=mean and bool(rng.random() < 0.3),
+                log_size=log_size)
+
+
+@pytest.mark.parametrize("case", range(160))
+def test_random_configs(lib, case):
+    """Seeded random geometries (1-9 frames, grids up to 20 x 20, 0-7 specials, 1-3 heads) and
+    forms with random options, in both score forms and both output types, against the oracle."""
+    import torch
+    from synth import make_log_sizes
+    rng = np.random.default_rng(1000 + case)
+    desc = _random_desc(rng)
+    prescale_q = bool(rng.random() < 0.5)
+    out_dtype = "bf16" if rng.random() < 0.3 else "fp32"
+    print(f"[random {case}] {desc} prescale_q={prescale_q} out={out_dtype}", flush=True)
+    q, k, v = inputs_for(desc, "bf16", seed=case)
+    plan = lib.Plan(**plan_kwargs(desc, "bf16", out_dtype), prescale_q=prescale_q)
+    out, ws = plan.new_output(), plan.new_workspace()
+    log_g = None
+    if desc.log_size:
+        _, log_g = make_log_sizes(desc.frames, desc.grid_h, desc.grid_w, desc.n_special, seed=case)
+        plan.forward_sized(to_device(q), to_device(k), to_device(v), torch.from_numpy(log_g).cuda(), out, ws)
+    else:
+        plan.forward(to_device(q), to_device(k), to_device(v), out, ws)
+    torch.cuda.synchronize()
+    ref = oracle.attention(q, k, v, desc, workers=4, log_g=log_g)
+    assert_close(out.float().cpu().numpy(), ref, fp32=False, label=f"random-{case}")
