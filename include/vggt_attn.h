@@ -39,6 +39,9 @@
  *     enqueued and vggt_attn_last_error() holds a description (thread-local).
  *   - Plans are immutable host objects: concurrent calls with one plan are safe as long as
  *     each call has its own workspace and output.
+ *   - The pack, attend and forward entry points enqueue kernel launches only (no memset, copy,
+ *     allocation or host synchronisation), so a caller may capture them into a HIP graph and
+ *     replay it; vggt_attn_copy_index_set copies to host memory and synchronises, so it may not.
  */
 #ifndef VGGT_ATTN_H
 #define VGGT_ATTN_H
