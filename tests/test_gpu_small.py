@@ -5,8 +5,8 @@ types, the exact and the f16 score form, plus the bit-exact index set and packed
 f16 packed keys), V = 1, determinism, a NaN-poisoned workspace, the rising-logit, spike and
 tied-Q/K stress inputs, the collapse identity (identical dropped rows under COUNT means equal
 dense attention), G2F's in-place reads stopping at the tensors' end, degenerate shapes (one
-token, one frame, nothing dropped, no specials), 160 seeded random configurations, and the C
-ABI's error codes.  Every call goes
+token, one frame, nothing dropped, no specials), 160 seeded random configurations on the bf16
+path and 40 on the float32 path, and the C ABI's error codes.  Every call goes
 through the C ABI of libvggt_attn.so."""
 import ctypes
 import zlib
@@ -526,3 +526,26 @@ def test_random_configs(lib, case):
     torch.cuda.synchronize()
     ref = oracle.attention(q, k, v, desc, workers=4, log_g=log_g)
     assert_close(out.float().cpu().numpy(), ref, fp32=False, label=f"random-{case}")
+
+
+@pytest.mark.parametrize("case", range(40))
+def test_random_configs_fp32(lib, case):
+    """The float32 path (float32 in and out) on seeded random geometries and forms, at the
+    float32 bar."""
+    import torch
+    from synth import make_log_sizes
+    rng = np.random.default_rng(7000 + case)  # (this seed range draws every form)
+    desc = _random_desc(rng)
+    print(f"[random fp32 {case}] {desc}", flush=True)
+    q, k, v = inputs_for(desc, "fp32", seed=500 + case)
+    plan = lib.Plan(**plan_kwargs(desc, "fp32", "fp32"))
+    out, ws = plan.new_output(), plan.new_workspace()
+    log_g = None
+    if desc.log_size:
+        _, log_g = make_log_sizes(desc.frames, desc.grid_h, desc.grid_w, desc.n_special, seed=500 + case)
+        plan.forward_sized(to_device(q), to_device(k), to_device(v), torch.from_numpy(log_g).cuda(), out, ws)
+    else:
+        plan.forward(to_device(q), to_device(k), to_device(v), out, ws)
+    torch.cuda.synchronize()
+    ref = oracle.attention(q, k, v, desc, workers=4, log_g=log_g)
+    assert_close(out.cpu().numpy(), ref, fp32=True, label=f"random-fp32-{case}")
