@@ -200,3 +200,27 @@ def test_f16_score_form_layout(va):
         assert plain["off_kpack"] == plain["off_kmax"]
     lay = va.Plan(4, 13, 11, 3, sigma=4, prescale_q=True, in_dtype="fp32").layout()
     assert lay["off_kpack"] == lay["off_kmax"]
+
+
+def test_alias_checks_come_before_any_device_call(va):
+    """Overlaps between out, the workspace and the inputs are refused (EALIAS) by forward, pack
+    and attend from the addresses alone, so fake (never dereferenced) addresses serve here.
+    Host-only: where a GPU is visible it is skipped, so that a regression in these checks could
+    never launch kernels on the fake addresses."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("fake device addresses: run on a host without a GPU")
+    L = va.lib()
+    p = va.Plan(4, 8, 8, 2, sigma=4, diag=True, mean=True)
+    nin = 2 * p.T * 64 * 2  # bf16 q/k/v bytes
+    nws = p.workspace_bytes
+    base = 1 << 40
+    q, k, v, out, ws = (base + i * (1 << 24) for i in range(5))
+    for call in ("forward", "attend"):
+        f = getattr(L, f"vggt_attn_{call}")
+        assert f(p.handle, q, k, v, k + 4096, ws, nws, None) == -5          # out inside k
+        assert f(p.handle, q, k, v, out, k + nin - 16, nws, None) == -5    # workspace over k's tail
+        assert f(p.handle, q, k, v, out, q, nws, None) == -5               # workspace on q
+        assert f(p.handle, q, k, v, ws + nws - 16, ws, nws, None) == -5    # out over the workspace's tail
+        assert b"overlaps" in L.vggt_attn_last_error()
+    assert L.vggt_attn_pack(p.handle, k, v, v + 16, nws, None) == -5

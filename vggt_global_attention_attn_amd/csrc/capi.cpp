@@ -189,6 +189,11 @@ int vggt_attn_attend(const vggt_attn_plan_t* plan, const void* q, const void* k,
   if (rc) return rc;
   if ((rc = check_workspace(*plan, workspace, workspace_bytes))) return rc;
   if ((rc = check_out_alias(*plan, q, k, v, out, workspace, workspace_bytes))) return rc;
+  // (the attention stage writes the split pieces' partial states into the workspace)
+  const size_t nin = tensor_bytes(*plan, plan->in_dtype);
+  if (overlaps(workspace, workspace_bytes, k, nin) || overlaps(workspace, workspace_bytes, v, nin) ||
+      overlaps(workspace, workspace_bytes, q, nin))
+    return set_error(VGGT_ATTN_EALIAS, "workspace overlaps q, k or v");
   hipError_t e = vggt::launch_attend(*plan, q, k, v, out, workspace, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_error(e, "attention kernel launch");
   return ok();
