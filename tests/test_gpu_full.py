@@ -6,8 +6,8 @@ Workloads: dense 32 frames (and G2M on the same tensors); SGA sigma 4 at 100 fra
 COUNT means); G2F, SGA sigma 9, and sigma 9 with the phase-shifted grid and a global COUNT
 mean on the same 200-frame tensors; SGA sigma 6 at 800 frames, with and without the phase
 shift.  All use 37x37 patches + 5 special tokens per frame, 16 heads, d = 64, bf16 inputs and
-fp32 output.  One gives every token a seeded group size of 1..4 (size-aware keys); the last runs
-G2F at the largest token count a plan accepts.  Names ending in -f16 run the f16 score form
+fp32 output.  One gives every token a seeded group size of 1..4 (size-aware keys); the last two
+run G2F and enhanced SGA sigma 9 at the largest token count a plan accepts.  Names ending in -f16 run the f16 score form
 (PRESCALE_Q: packed keys f16(k * 2^-e_h), Q * tau * log2(e) * 2^e_h rounded to f16 once).  A separate test runs the 800-frame sigma 6
 workload on the tied-Q/K stress input with bf16 output."""
 import numpy as np
@@ -38,7 +38,12 @@ FULL = [
     # the largest plan the library accepts: T = 7,999,428 tokens (limit 8,000,000); with 6 heads
     # an [H][T][64] tensor holds 3.07e9 elements, so every offset needs 64 bits
     ("g2f-5822f-max", Desc(5822, 37, 37, 6, g2f=True)),
+    # the global path at the same size (same tensors): 1,014,228 + 5,821 packed keys, 249,984
+    # work items whose sparse last round runs as 4 key-range pieces and the merge
+    ("sga9-5822f-max", Desc(5822, 37, 37, 6, sigma=9, diag=True, mean=True)),
 ]
+# sampled rows per workload (4096 unless listed: each of these rows attends to a million keys)
+ROWS = {"sga9-5822f-max": 512}
 
 _cache = {}
 _refs = {}  # oracle rows of the last workload, shared by its exact and f16 score-form cases
@@ -83,7 +88,7 @@ def test_full_size_sampled_rows(name, desc):
         idx, dcount = plan.index_set(ws)
         assert np.array_equal(idx, oracle.index_set(desc))
         assert np.array_equal(dcount, oracle.dropped_counts(desc).astype(np.int32))
-    rows = sample_rows(desc.frames, desc.grid_h, desc.grid_w, desc.n_special, count=4096, seed=1)
+    rows = sample_rows(desc.frames, desc.grid_h, desc.grid_w, desc.n_special, count=ROWS.get(name, 4096), seed=1)
     got = out[:, torch.from_numpy(rows).cuda()].double().cpu().numpy()
     del out, ws
     base = name[:-len("-f16")] if name.endswith("-f16") else name
@@ -116,7 +121,7 @@ def test_full_size_tied_qk_bf16_out():
     plan.forward(up(q), up(k), up(v), out, ws)
     torch.cuda.synchronize()
     assert bool(torch.isfinite(out.float()).all())
-    rows = sample_rows(desc.frames, desc.grid_h, desc.grid_w, desc.n_special, count=4096, seed=1)
+    rows = sample_rows(desc.frames, desc.grid_h, desc.grid_w, desc.n_special, count=ROWS.get(name, 4096), seed=1)
     got = out[:, torch.from_numpy(rows).cuda()].double().cpu().numpy()
     del out, ws
     print(f"[full] tied-qk: oracle on {rows.size} rows", flush=True)
