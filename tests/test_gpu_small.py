@@ -465,6 +465,8 @@ EDGE = [
     (Desc(3, 9, 8, 1, n_special=0, sigma=9, diag=True, mean=True, mean_count=True), "no-specials-sga9"),
     (Desc(2, 2, 65, 1, n_special=0, sigma=2, diag=True, mean=True, ref_dense=False), "wide-grid-pi3"),
     (Desc(3, 13, 11, 1, n_special=7, sigma=6, diag=True, mean=True, phase_shift=True), "seven-specials-phase"),
+    (Desc(2, 2, 2, 4096, n_special=1, sigma=4, diag=True, mean=True), "max-heads"),  # the largest head count
+    (Desc(2, 2, 3, 4096, n_special=1, g2f=True), "max-heads-g2f"),
 ]
 
 
@@ -473,7 +475,8 @@ EDGE = [
 def test_edge_shapes(lib, desc, label, prescale_q):
     """Degenerate geometries: a single token (softmax over one key: out = v), a single frame
     (everything dense), one-patch frames (no dropped patch, so no diagonal or mean term), no
-    special tokens, a grid one row high, more specials than usual; exact and f16 score forms."""
+    special tokens, a grid one row high, more specials than usual, the largest head count a plan
+    accepts (4096); exact and f16 score forms."""
     q, k, v = inputs_for(desc, "bf16", seed=31)
     _, got, _, _ = run(lib, desc, q, k, v, prescale_q=prescale_q)
     ref = oracle.attention(q, k, v, desc, workers=4)
