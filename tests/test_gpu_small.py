@@ -384,6 +384,26 @@ def test_parity_log_size_fp32(lib, desc, label):
     assert_close(got, ref, fp32=True, label=label)
 
 
+@pytest.mark.parametrize("desc,label", [(Desc(6, 13, 11, 2, sigma=4, diag=True, log_size=True), "sga4-sized-extreme"),
+                                        (Desc(5, 37, 37, 2, sigma=6, diag=True, log_size=True), "sga6-sized-extreme-37x37"),
+                                        (Desc(3, 37, 37, 2, g2f=True, log_size=True), "g2f-sized-extreme-37x37")],
+                         ids=["sga4", "sga6-37x37", "g2f-37x37"])
+def test_log_size_extreme(lib, desc, label):
+    """Sizes far outside 1..4: a few tokens late in the key range stand for up to e^25 tokens
+    (each pulls its row's running max up by tens of octaves mid-stream, through the rescale
+    path), one group of tokens is fractional (ln g = -20), the rest stay small."""
+    from synth import make_log_sizes
+    q, k, v = inputs_for(desc, "bf16", seed=41)
+    _, lg = make_log_sizes(desc.frames, desc.grid_h, desc.grid_w, desc.n_special, seed=7)
+    rng = np.random.default_rng(41)
+    late = rng.choice(np.arange(desc.T // 2, desc.T), size=6, replace=False)
+    lg[late] = np.array([25.0, 12.5, 7.0, 18.0, 3.0, 21.0], dtype=np.float32)
+    lg[rng.choice(desc.T // 2, size=4, replace=False)] = -20.0
+    got = run_sized(lib, desc, q, k, v, lg)
+    ref = oracle.attention(q, k, v, desc, workers=4, log_g=lg)
+    assert_close(got, ref, fp32=False, label=label)
+
+
 def test_log_size_zero_sizes_equal_plain_path(lib):
     """log g = 0 everywhere: the size-aware kernel must give the plain kernel's bits."""
     desc = Desc(6, 13, 11, 2, sigma=6, diag=True, log_size=True)
