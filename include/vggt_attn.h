@@ -214,6 +214,23 @@ int vggt_attn_pack_sized(const vggt_attn_plan_t* plan, const void* k, const void
                          const float* log_g, void* workspace, size_t workspace_bytes,
                          void* stream);
 
+/* vggt_attn_forward for callers that cannot allocate device memory or pass a workspace --
+ * code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.  The
+ * workspace is a static device array inside the library, 256 MiB (268,435,456 bytes) on each GPU
+ * the library runs on, held from the library's load until the process ends; its device address
+ * is looked up once per device on the first call (a host-side lookup, no allocation).  The call
+ * itself allocates and frees nothing and only enqueues kernels on `stream`.
+ *   - Plans whose vggt_attn_workspace_bytes() exceeds 268,435,456 are refused with ENOSPC
+ *     (800 frames of 1374 tokens at 16 heads need about 800 MiB: use vggt_attn_forward).
+ *   - LOG_SIZE plans are refused (EINVAL).  Tensor checks as for vggt_attn_forward.
+ *   - Every call on one GPU uses that GPU's single array, which keeps the last call's
+ *     contents (no part of it needs to start cleared: the pack stage writes everything the
+ *     attention stage reads).  Calls that can run at the same time on one GPU -- on different
+ *     streams, or from several host threads without ordering -- race on it and give undefined
+ *     results; calls on one stream are ordered and safe. */
+int vggt_attn_forward_noalloc(const vggt_attn_plan_t* plan, const void* q, const void* k,
+                              const void* v, void* out, void* stream);
+
 /* Copy S (|S| int32, ascending token ids) and |D_f| (N int32) from a packed workspace to host
  * memory; waits for `stream`.  Either host pointer may be NULL.  Under G2F there is no S and
  * host_idx is left untouched. */

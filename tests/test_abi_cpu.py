@@ -202,6 +202,21 @@ def test_f16_score_form_layout(va):
     assert lay["off_kpack"] == lay["off_kmax"]
 
 
+def test_noalloc_refuses_large_plans_before_any_device_call(va):
+    """vggt_attn_forward_noalloc checks the plan's workspace against its static 256 MiB before it
+    looks at a device: the 800-frame workload (about 800 MiB) gets ENOSPC with the sizes named,
+    and LOG_SIZE plans get EINVAL (no tensor pointer is needed to reach either answer)."""
+    L = va.lib()
+    assert L.vggt_attn_forward_noalloc(None, None, None, None, None, None) == -1
+    big = va.Plan(800, 37, 37, 16, sigma=6, diag=True, mean=True)
+    assert big.workspace_bytes > 256 << 20
+    assert L.vggt_attn_forward_noalloc(big.handle, None, None, None, None, None) == -3
+    msg = L.vggt_attn_last_error().decode()
+    assert str(big.workspace_bytes) in msg and str(256 << 20) in msg
+    sized = va.Plan(4, 8, 8, 2, sigma=4, diag=True, log_size=True)
+    assert L.vggt_attn_forward_noalloc(sized.handle, None, None, None, None, None) == -1
+
+
 def test_alias_checks_come_before_any_device_call(va):
     """Overlaps between out, the workspace and the inputs are refused (EALIAS) by forward, pack
     and attend from the addresses alone, so fake (never dereferenced) addresses serve here.

@@ -20,7 +20,8 @@ STATUS = {0: "OK", -1: "EINVAL", -2: "EUNSUPPORTED", -3: "ENOSPC", -4: "EALIGN",
 
 EXPORTS = ("vggt_attn_plan", "vggt_attn_plan_destroy", "vggt_attn_workspace_bytes", "vggt_attn_counts",
            "vggt_attn_layout", "vggt_attn_forward", "vggt_attn_pack", "vggt_attn_attend",
-           "vggt_attn_forward_sized", "vggt_attn_pack_sized", "vggt_attn_copy_index_set", "vggt_attn_last_error")
+           "vggt_attn_forward_sized", "vggt_attn_pack_sized", "vggt_attn_forward_noalloc", "vggt_attn_copy_index_set",
+           "vggt_attn_last_error")
 
 
 class VggtAttnError(RuntimeError):
@@ -72,6 +73,8 @@ def lib() -> ctypes.CDLL:
     L.vggt_attn_forward_sized.restype = ctypes.c_int
     L.vggt_attn_pack_sized.argtypes = [vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     L.vggt_attn_pack_sized.restype = ctypes.c_int
+    L.vggt_attn_forward_noalloc.argtypes = [vp, vp, vp, vp, vp, vp]
+    L.vggt_attn_forward_noalloc.restype = ctypes.c_int
     L.vggt_attn_copy_index_set.argtypes = [vp, vp, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32), vp]
     L.vggt_attn_copy_index_set.restype = ctypes.c_int
     L.vggt_attn_last_error.argtypes = []
@@ -188,6 +191,14 @@ class Plan:
         _check(lib().vggt_attn_forward(self._h, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(workspace),
                                        workspace.numel() * workspace.element_size(),
                                        _stream_handle(stream, q.device)))
+
+    def forward_noalloc(self, q, k, v, out, stream=None) -> None:
+        """vggt_attn_forward on the library's static per-GPU workspace (no workspace argument)."""
+        for t, n in ((q, "q"), (k, "k"), (v, "v")):
+            self._check_tensor(t, n, self.in_dtype)
+        self._check_tensor(out, "out", self.out_dtype)
+        _check(lib().vggt_attn_forward_noalloc(self._h, _ptr(q), _ptr(k), _ptr(v), _ptr(out),
+                                               _stream_handle(stream, q.device)))
 
     def _check_log_g(self, log_g) -> None:
         import torch

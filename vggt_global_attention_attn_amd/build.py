@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libvggt_attn.so")
 
-HIP_SOURCES = ["pack.hip", "attn.hip"]
+HIP_SOURCES = ["pack.hip", "attn.hip", "scratch.hip"]
 CXX_SOURCES = ["plan.cpp", "capi.cpp"]
 ARCH = "gfx950"
 

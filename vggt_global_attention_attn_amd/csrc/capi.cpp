@@ -214,6 +214,20 @@ int vggt_attn_forward_sized(const vggt_attn_plan_t* plan, const void* q, const v
   return forward_impl(*plan, q, k, v, log_g, out, workspace, workspace_bytes, stream);
 }
 
+int vggt_attn_forward_noalloc(const vggt_attn_plan_t* plan, const void* q, const void* k, const void* v,
+                              void* out, void* stream) {
+  if (!plan) return set_error(VGGT_ATTN_EINVAL, "plan is NULL");
+  if (int rc = no_log_size(*plan)) return rc;
+  if (size_t(plan->layout.total_bytes) > vggt::kScratchBytes)
+    return set_error(VGGT_ATTN_ENOSPC, "plan needs " + std::to_string(plan->layout.total_bytes) +
+                                           " bytes of workspace; the no-allocation entry point has " +
+                                           std::to_string(vggt::kScratchBytes) + " (use vggt_attn_forward)");
+  void* ws = nullptr;
+  const hipError_t e = vggt::scratch_address(&ws);
+  if (e != hipSuccess) return hip_error(e, "static workspace address");
+  return forward_impl(*plan, q, k, v, nullptr, out, ws, vggt::kScratchBytes, stream);
+}
+
 int vggt_attn_copy_index_set(const vggt_attn_plan_t* plan, const void* workspace,
                              int32_t* host_idx, int32_t* host_dcount, void* stream) {
   if (!plan || !workspace) return set_error(VGGT_ATTN_EINVAL, "NULL argument");

@@ -23,4 +23,8 @@ hipError_t launch_size_bias(const vggt_attn_plan_s& p, const float* log_g, void*
 hipError_t launch_attend(const vggt_attn_plan_s& p, const void* q, const void* k, const void* v,
                          void* out, void* ws, hipStream_t stream);
 
+// Device address, on the current device, of the static workspace of the no-allocation entry
+// point (kScratchBytes bytes); looked up once per device.
+hipError_t scratch_address(void** out);
+
 }  // namespace vggt

@@ -44,6 +44,8 @@ constexpr int kMaxSplit = 8;
 // has its own L2.  Used only to order work items; correctness does not depend on it.
 constexpr int kXcds = 8;
 constexpr int kPartRow = 68;  // floats per query row of a piece: O[64], m, l, 2 unused
+// Size of the static device workspace of vggt_attn_forward_noalloc (one copy per GPU).
+constexpr size_t kScratchBytes = size_t(256) << 20;
 
 // Geometry the device code needs to enumerate S and the mean frames and to test membership in
 // closed form.  Compressed frame f has grid phase k = f mod nphase (nphase = s_h*s_w with the
