@@ -32,14 +32,23 @@
 #include "launch.h"
 
 
+// Row-sum method of the bf16 kernel: 0 = matrix cores in the exact-scale forms without key
+// biases, VALU dot2 in the others (the default), 1 = matrix cores everywhere, 2 = VALU dot2
+// everywhere (for timing comparisons).
+#ifndef VGGT_SUM_MODE
+#define VGGT_SUM_MODE 0
+#endif
+
 namespace vggt {
 namespace {
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
 typedef short i16x8_t __attribute__((ext_vector_type(8)));
 // s_waitcnt immediate for vmcnt(0) with expcnt and lgkmcnt left at their maxima (gfx9 encoding).
 constexpr int kWaitVmcnt0 = 0x0F70;
+constexpr bf16x2_t kOnes2 = {(__bf16)1.0f, (__bf16)1.0f};
 // Word 3 of a raw buffer descriptor on gfx9-family parts (gfx950 included): 32-bit data format,
 // no swizzle, so that offsets are plain byte offsets range-checked against num_records.
 constexpr int kBufferWord3 = 0x00020000;
@@ -224,12 +233,18 @@ void attn_bf16_kernel(AttnArgs a) {
   // from it.  Before tile 0 the slot holds the diagonal term's logit (raw or log2 units).
   float m_run[QB];
   f32x4_t o[QB][4];
-  // Row sums on the matrix cores: l^T += 1 P^T with an all-ones A operand, two 16x16x32
-  // products per block beside the 8 of PV, so every lane holds its query's whole sum (4 equal
-  // copies).  The VALU dot2 instructions that could sum P instead run on the matrix pipe of
-  // gfx950: each one waits for the MFMA in flight to drain, so 8 of them per block cost more
-  // than these two products (measured: 812 -> 800 ms at 800 frames, 7.5 -> 7.3 ms dense).
+  // Row sums, two ways.  kMfmaSum: on the matrix cores, l^T += 1 P^T with an all-ones A operand,
+  // two 16x16x32 products per block beside the 8 of PV, so every lane holds its query's whole
+  // sum (4 equal copies).  Else: VALU dot2 instructions into a lane-partial sum (summed over the
+  // lane group at the end).  The dot2 instructions run on the matrix pipe of gfx950 -- each one
+  // waits for the MFMA in flight to drain -- so the products win where the registers allow them:
+  // the exact scale at 800 frames (830 -> 818 ms in one session, 800 -> 789 in another) and
+  // dense (7.24 -> 6.95 ms).  The f16 score form (its chain-start tuples stay live) and the
+  // size-aware keys (bias tiles) spill into their loops with the 12 extra registers and keep
+  // dot2 (787 against 811 ms and 877 against 890 ms at 800 frames).
+  constexpr bool kMfmaSum = VGGT_SUM_MODE == 1 || (VGGT_SUM_MODE == 0 && !PRESCALE_Q && !LOGSIZE);
   f32x4_t l_acc[QB];
+  float l_run[QB];
   const bf16x8_t ones8 = {(__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f,
                           (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f, (__bf16)1.0f};
   // Two ways to reach log2 units.  Exact (default): Q is used as given, scores are in units of
@@ -401,6 +416,7 @@ void attn_bf16_kernel(AttnArgs a) {
     const float off = m_run[qb];
     auto e = [&](float x) { return (__bf16)__builtin_amdgcn_exp2f(PRESCALE_Q ? x : fmaf(x, c, off)); };
     uint32_t bits = 0;
+    float l = l_run[qb];
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2) {
       const f32x4_t& s0 = s[2 * h2];
@@ -409,7 +425,14 @@ void attn_bf16_kernel(AttnArgs a) {
       pf[h2] = pv;
       const uint4 w = __builtin_bit_cast(uint4, pv);
       bits |= w.x | w.y | w.z | w.w;
+      if constexpr (!kMfmaSum) {
+        l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pv, pv, 0, 1), kOnes2, l, false);
+        l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pv, pv, 2, 3), kOnes2, l, false);
+        l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pv, pv, 4, 5), kOnes2, l, false);
+        l = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pv, pv, 6, 7), kOnes2, l, false);
+      }
     }
+    if constexpr (!kMfmaSum) l_run[qb] = l;
     return bits;
   };
   auto accumulate_qb = [&](const bf16x8_t (&vf)[4][2], int qb, const bf16x8_t (&pf)[2]) {
@@ -418,8 +441,10 @@ void attn_bf16_kernel(AttnArgs a) {
       o[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[db][0], pf[0], o[qb][db], 0, 0, 0);
       o[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[db][1], pf[1], o[qb][db], 0, 0, 0);
     }
-    l_acc[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones8, pf[0], l_acc[qb], 0, 0, 0);
-    l_acc[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones8, pf[1], l_acc[qb], 0, 0, 0);
+    if constexpr (kMfmaSum) {
+      l_acc[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones8, pf[0], l_acc[qb], 0, 0, 0);
+      l_acc[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones8, pf[1], l_acc[qb], 0, 0, 0);
+    }
   };
   // Softmax of query block qb of the tile in hand, with the block's next-tile scores formed on
   // the matrix cores in the same stretch of code.  Lazy running max: weights are taken against
@@ -428,6 +453,7 @@ void attn_bf16_kernel(AttnArgs a) {
   auto block = [&](const bf16x8_t (&kf)[4][2], const float* bb, int qb, f32x4_t (&s_cur)[4],
                    f32x4_t (&s_next)[4], bf16x8_t (&pf)[2], bool next) {
     if (next) scores_qb(kf, bb, qb, s_next, m_run[qb]);
+    const float l_prev = l_run[qb];
     const uint32_t bits = probs_qb(qb, s_cur, pf);
     // (expected false: the rescale is laid out of line, so the common path runs straight on)
     if (__builtin_expect(__builtin_amdgcn_ballot_w64((bits & 0x40004000u) != 0) != 0, 0)) {
@@ -439,7 +465,8 @@ void attn_bf16_kernel(AttnArgs a) {
       const float d = PRESCALE_Q ? vmax(mx + shift, 0.f) : vmax(m_run[qb] - fmaf(-mx, c, -shift), 0.f);
       const float alpha = __builtin_amdgcn_exp2f(-d);
       m_run[qb] -= d;
-      l_acc[qb] *= alpha;  // (this block's weights are added only after the check)
+      if constexpr (kMfmaSum) l_acc[qb] *= alpha;  // (this block's weights are added after the check)
+      else l_run[qb] = l_prev * alpha;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         o[qb][k] *= alpha;
@@ -505,7 +532,10 @@ void attn_bf16_kernel(AttnArgs a) {
       if (self) dot += a.logsize[t] * a.size_scale;
     }
     m_run[qb] = self ? dot : -INFINITY;
-    l_acc[qb] = self ? f32x4_t{shift_scale, shift_scale, shift_scale, shift_scale} : f32x4_t{0.f, 0.f, 0.f, 0.f};
+    if constexpr (kMfmaSum)
+      l_acc[qb] = self ? f32x4_t{shift_scale, shift_scale, shift_scale, shift_scale} : f32x4_t{0.f, 0.f, 0.f, 0.f};
+    else
+      l_run[qb] = (self && grp == 0) ? shift_scale : 0.f;
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
       f32x4_t init = {0.f, 0.f, 0.f, 0.f};
@@ -600,7 +630,8 @@ void attn_bf16_kernel(AttnArgs a) {
     const float m_new = vmax(m_run[qb], row_max(sa[qb]));  // finite: tile 0 holds a valid key
     if constexpr (!INPLACE) {  // (without a diagonal term l and O are still zero)
       const float alpha = __builtin_amdgcn_exp2f((m_run[qb] - m_new) * sc);
-      l_acc[qb] *= alpha;
+      if constexpr (kMfmaSum) l_acc[qb] *= alpha;
+      else l_run[qb] *= alpha;
 #pragma unroll
       for (int k = 0; k < 4; ++k) o[qb][k] *= alpha;
     }
@@ -634,7 +665,7 @@ void attn_bf16_kernel(AttnArgs a) {
     float* dst = a.part + size_t(blockIdx.x) * BM * kPartRow;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      const float l = l_acc[qb][0];
+      const float l = kMfmaSum ? l_acc[qb][0] : group_sum(l_run[qb]);
       float* row = dst + size_t(wave * WQ + qb * 16 + l16) * kPartRow;
 #pragma unroll
       for (int db = 0; db < 4; ++db) *reinterpret_cast<f32x4_t*>(row + db * 16 + grp * 4) = o[qb][db];
@@ -647,7 +678,7 @@ void attn_bf16_kernel(AttnArgs a) {
   }
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    const float l = l_acc[qb][0];
+    const float l = kMfmaSum ? l_acc[qb][0] : group_sum(l_run[qb]);
     const float inv = __builtin_amdgcn_rcpf(l);
     const int64_t t = wrow0 + qb * 16 + l16;
     if (t >= row_end) continue;
