@@ -35,8 +35,13 @@
  *     except as documented for vggt_attn_pack / vggt_attn_copy_index_set.
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).  Device work is
  *     only enqueued; execution errors surface at the caller's next synchronisation.
- *   - Every int-returning call returns a vggt_attn_status (0 = success).  On failure nothing is
- *     enqueued and vggt_attn_last_error() holds a description (thread-local).
+ *   - Every int-returning call returns a vggt_attn_status (0 = success) and on failure
+ *     vggt_attn_last_error() holds a description (thread-local).  Every argument and plan check
+ *     comes before the first launch, so a failure other than EHIP enqueues nothing.  EHIP means
+ *     a launch was refused by the runtime; a call that launches several kernels (the pack stage:
+ *     means, then pack; the attention stage: main kernel, split pieces, merge) may then have
+ *     enqueued the kernels before the refused one, and the output and workspace contents are
+ *     undefined until a later call succeeds.
  *   - Plans are immutable host objects: concurrent calls with one plan are safe as long as
  *     each call has its own workspace and output.
  *   - The pack, attend and forward entry points enqueue kernel launches only (no memset, copy,
@@ -173,7 +178,11 @@ int vggt_attn_counts(const vggt_attn_plan_t* plan, int64_t* n_kv, int64_t* n_mea
 int vggt_attn_layout(const vggt_attn_plan_t* plan, vggt_attn_layout_t* out);
 
 /* Full forward: vggt_attn_pack followed by vggt_attn_attend on `stream` (not for LOG_SIZE plans:
- * see vggt_attn_forward_sized).
+ * see vggt_attn_forward_sized).  Computes, for every query token t and head h, out[h][t] =
+ * sum_j w_j v_j with w = softmax over the plan's keys of tau * <q_t, k_j> (tau = 1/sqrt(d)), one
+ * normalisation over the kept set S, the diagonal self term and the mean keys together (AVGGT
+ * notes, 关键设计 2, the attention equation restricted to S; 关键设计 3, the three terms under a
+ * single softmax; 关键设计 1, G2F keys = the query's own frame).
  * q, k, v: [H][T][d] of the input dtype; out: [H][T][d] of the output dtype; every pointer
  * 16-byte aligned; out must not overlap q, k, v or the workspace (EALIAS). */
 int vggt_attn_forward(const vggt_attn_plan_t* plan, const void* q, const void* k, const void* v,
@@ -192,7 +201,9 @@ int vggt_attn_forward(const vggt_attn_plan_t* plan, const void* q, const void* k
 int vggt_attn_pack(const vggt_attn_plan_t* plan, const void* k, const void* v, void* workspace,
                    size_t workspace_bytes, void* stream);
 
-/* Attention stage on a workspace already filled by vggt_attn_pack for the same plan and the
+/* Attention stage (AVGGT notes, 关键设计 2 and 3: softmax(tau Q K^T) V over the packed keys,
+ * the diagonal self term and the mean keys in one normalisation; 关键设计 1 for G2F) on a
+ * workspace already filled by vggt_attn_pack for the same plan and the
  * same k, v (k and v are read again for the diagonal term, and for every key by bf16 G2F
  * plans without PRESCALE_Q, which keep no packed copy).  Writes every element of out.  It
  * uses the workspace's off_part area as scratch (the partial softmax states of a split last
@@ -231,9 +242,27 @@ int vggt_attn_pack_sized(const vggt_attn_plan_t* plan, const void* k, const void
 int vggt_attn_forward_noalloc(const vggt_attn_plan_t* plan, const void* q, const void* k,
                               const void* v, void* out, void* stream);
 
+/* Models whose global-layer schedule vggt_attn_layer_schedule knows. */
+enum { VGGT_ATTN_MODEL_VGGT = 0, VGGT_ATTN_MODEL_PI3 = 1 };
+
+/* The form of global layer `layer` (0..23) under AVGGT (AVGGT notes, 整体框架: the 24 global
+ * layers, numbered 0-23, fall into an early part converted to Global-to-Frame -- indices below
+ * t_early, 9 for VGGT and 10 for pi^3 --, a middle part that keeps global attention with K/V
+ * subsampled by sigma and the diagonal and mean terms, and a late part kept unchanged; the
+ * ablation table's row AVGGT(2)- names the late part as layers 20-23).  Host only.
+ * Writes the sigma and flags to pass to vggt_attn_plan: G2F (sigma 1) for an early layer;
+ * sigma with DIAG | MEAN, plus REF_DENSE for VGGT (frame 0 kept dense; pi^3 compresses every
+ * frame, 关键设计 2), for a middle layer; sigma 1 and no flag (dense) for a late layer.
+ * model: VGGT_ATTN_MODEL_VGGT or VGGT_ATTN_MODEL_PI3; sigma in {1, 2, 4, 6, 9} (1 keeps the
+ * middle layers dense); layer in [0, 24).  Anything else: EINVAL.  Either output may be NULL. */
+int vggt_attn_layer_schedule(int model, int layer, int sigma, int* out_sigma, unsigned* out_flags);
+
 /* Copy S (|S| int32, ascending token ids) and |D_f| (N int32) from a packed workspace to host
- * memory; waits for `stream`.  Either host pointer may be NULL.  Under G2F there is no S and
- * host_idx is left untouched. */
+ * memory; waits for `stream`.  S is the kept set of AVGGT notes 关键设计 2 (the first patch of
+ * each s_h x s_w window of every compressed frame, every special token, every token of a dense
+ * frame; RegimeVGGT notes 关键设计 3 for the phase-shifted grid); |D_f| counts the patches of
+ * frame f outside S, the tokens its mean key stands for (关键设计 3).  Either host pointer may be
+ * NULL.  Under G2F there is no S and host_idx is left untouched. */
 int vggt_attn_copy_index_set(const vggt_attn_plan_t* plan, const void* workspace,
                              int32_t* host_idx, int32_t* host_dcount, void* stream);
 

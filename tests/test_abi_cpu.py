@@ -239,3 +239,43 @@ def test_alias_checks_come_before_any_device_call(va):
         assert f(p.handle, q, k, v, ws + nws - 16, ws, nws, None) == -5    # out over the workspace's tail
         assert b"overlaps" in L.vggt_attn_last_error()
     assert L.vggt_attn_pack(p.handle, k, v, v + 16, nws, None) == -5
+
+
+def test_layer_schedule_follows_avggt(va):
+    """AVGGT notes, 整体框架: the 24 global layers are numbered 0-23; indices below t_early (9 for
+    VGGT, i.e. layers 0-8; 10 for pi^3) become Global-to-Frame, the middle layers keep global
+    attention with K/V subsampled by sigma (with the diagonal and mean terms of 关键设计 3, the
+    flowchart's SGA branch), and the late layers stay unchanged; the ablation table's row
+    AVGGT(2)- ("late layers (20-23) also to frame attention") fixes the late part as 20-23.
+    VGGT keeps frame 0 dense, pi^3 compresses every frame (关键设计 2)."""
+    for model, t_early, ref in (("vggt", 9, True), ("pi3", 10, False)):
+        for sigma in (2, 4, 6, 9):
+            s = va.layer_schedule(model, sigma)
+            assert len(s) == 24
+            for layer, kw in enumerate(s):
+                if layer < t_early:
+                    assert kw == dict(sigma=1, g2f=True, ref_dense=False, diag=False, mean=False), (model, layer)
+                elif layer < 20:
+                    assert kw == dict(sigma=sigma, g2f=False, ref_dense=ref, diag=True, mean=True), (model, layer)
+                else:
+                    assert kw == dict(sigma=1, g2f=False, ref_dense=False, diag=False, mean=False), (model, layer)
+    # sigma 1 keeps the middle layers dense
+    assert all(kw["sigma"] == 1 and not kw["diag"] for kw in va.layer_schedule("vggt", 1)[9:])
+    L = va.lib()
+    import ctypes
+    for model, layer, sigma in ((2, 0, 9), (0, 24, 9), (0, -1, 9), (1, 5, 3)):
+        assert L.vggt_attn_layer_schedule(model, layer, sigma, None, None) == -1
+    s, f = ctypes.c_int(), ctypes.c_uint()
+    assert L.vggt_attn_layer_schedule(0, 8, 6, ctypes.byref(s), ctypes.byref(f)) == 0 and f.value == va.G2F
+    assert L.vggt_attn_layer_schedule(0, 9, 6, ctypes.byref(s), ctypes.byref(f)) == 0 and s.value == 6
+    assert f.value == va.DIAG | va.MEAN | va.REF_DENSE
+
+
+def test_scheduled_layers_share_plans(va):
+    """The scheduled driver builds one plan per distinct form (G2F, SGA, dense) and reports the
+    pass's FLOPs as the sum over the 24 layers of each layer's plan."""
+    sl = va.ScheduledLayers(6, 13, 11, 2, model="vggt", sigma=4, device="cpu")
+    assert len(sl.plans) == 3
+    assert sl.index[:9] == [sl.index[0]] * 9 and len(set(sl.index[9:20])) == 1 and len(set(sl.index[20:])) == 1
+    per = [p.counts()["flops"] for p in sl.plans]
+    assert sl.flops() == 9 * per[sl.index[0]] + 11 * per[sl.index[9]] + 4 * per[sl.index[20]]

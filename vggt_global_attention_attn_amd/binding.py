@@ -21,7 +21,9 @@ STATUS = {0: "OK", -1: "EINVAL", -2: "EUNSUPPORTED", -3: "ENOSPC", -4: "EALIGN",
 EXPORTS = ("vggt_attn_plan", "vggt_attn_plan_destroy", "vggt_attn_workspace_bytes", "vggt_attn_counts",
            "vggt_attn_layout", "vggt_attn_forward", "vggt_attn_pack", "vggt_attn_attend",
            "vggt_attn_forward_sized", "vggt_attn_pack_sized", "vggt_attn_forward_noalloc", "vggt_attn_copy_index_set",
-           "vggt_attn_last_error")
+           "vggt_attn_layer_schedule", "vggt_attn_last_error")
+MODELS = {"vggt": 0, "pi3": 1}
+GLOBAL_LAYERS = 24
 
 
 class VggtAttnError(RuntimeError):
@@ -75,6 +77,9 @@ def lib() -> ctypes.CDLL:
     L.vggt_attn_pack_sized.restype = ctypes.c_int
     L.vggt_attn_forward_noalloc.argtypes = [vp, vp, vp, vp, vp, vp]
     L.vggt_attn_forward_noalloc.restype = ctypes.c_int
+    L.vggt_attn_layer_schedule.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_int),
+                                           ctypes.POINTER(ctypes.c_uint)]
+    L.vggt_attn_layer_schedule.restype = ctypes.c_int
     L.vggt_attn_copy_index_set.argtypes = [vp, vp, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32), vp]
     L.vggt_attn_copy_index_set.restype = ctypes.c_int
     L.vggt_attn_last_error.argtypes = []
@@ -253,6 +258,55 @@ class Plan:
             self._h, _ptr(workspace), idx.ctypes.data_as(i32p) if idx.size else None,
             dcount.ctypes.data_as(i32p), _stream_handle(stream, workspace.device)))
         return idx, dcount
+
+
+def layer_schedule(model: str = "vggt", sigma: int = 9) -> list:
+    """The plan keyword arguments (sigma and form flags) of each of the 24 global layers under
+    AVGGT's schedule, as vggt_attn_layer_schedule gives them; combine each with the geometry
+    (frames, grid_h, grid_w, heads) to build that layer's Plan."""
+    L = lib()
+    out = []
+    for layer in range(GLOBAL_LAYERS):
+        s, f = ctypes.c_int(), ctypes.c_uint()
+        _check(L.vggt_attn_layer_schedule(MODELS[model], layer, sigma, ctypes.byref(s), ctypes.byref(f)))
+        fl = f.value
+        out.append(dict(sigma=s.value, g2f=bool(fl & G2F), ref_dense=bool(fl & REF_DENSE), diag=bool(fl & DIAG),
+                        mean=bool(fl & MEAN)))
+    return out
+
+
+class ScheduledLayers:
+    """The global layers of one model run under AVGGT's schedule on one geometry: the distinct
+    plans (G2F, SGA sigma with the diagonal and mean terms, dense) built once and shared by the
+    layers that use them, with a workspace each.  forward(layer, ...) runs that layer's form."""
+
+    def __init__(self, frames: int, grid_h: int, grid_w: int, heads: int, model: str = "vggt", sigma: int = 9,
+                 n_special: int = 5, in_dtype: str = "bf16", out_dtype: str = "fp32", device="cuda"):
+        self.kinds = layer_schedule(model, sigma)
+        self.plans, self.workspaces, self.index = [], [], []
+        seen = {}
+        for kw in self.kinds:
+            key = tuple(sorted(kw.items()))
+            if key not in seen:
+                seen[key] = len(self.plans)
+                self.plans.append(Plan(frames, grid_h, grid_w, heads, n_special=n_special, in_dtype=in_dtype,
+                                       out_dtype=out_dtype, **kw))
+                self.workspaces.append(None)
+            self.index.append(seen[key])
+        self.device = device
+
+    def plan(self, layer: int) -> Plan:
+        return self.plans[self.index[layer]]
+
+    def forward(self, layer: int, q, k, v, out, stream=None) -> None:
+        i = self.index[layer]
+        if self.workspaces[i] is None:
+            self.workspaces[i] = self.plans[i].new_workspace(self.device)
+        self.plans[i].forward(q, k, v, out, self.workspaces[i], stream)
+
+    def flops(self) -> float:
+        """Algorithmic FLOPs of one pass over the 24 layers."""
+        return sum(self.plan(layer).counts()["flops"] for layer in range(GLOBAL_LAYERS))
 
 
 def attention(q, k, v, plan: Plan, stream=None, log_g=None):

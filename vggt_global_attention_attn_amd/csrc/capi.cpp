@@ -228,6 +228,30 @@ int vggt_attn_forward_noalloc(const vggt_attn_plan_t* plan, const void* q, const
   return forward_impl(*plan, q, k, v, nullptr, out, ws, vggt::kScratchBytes, stream);
 }
 
+int vggt_attn_layer_schedule(int model, int layer, int sigma, int* out_sigma, unsigned* out_flags) {
+  // AVGGT notes, 整体框架: t_early = 9 (VGGT) or 10 (pi^3); ablation row AVGGT(2)-: late = 20..23.
+  constexpr int kGlobalLayers = 24, kLateFrom = 20;
+  int t_early;
+  if (model == VGGT_ATTN_MODEL_VGGT) t_early = 9;
+  else if (model == VGGT_ATTN_MODEL_PI3) t_early = 10;
+  else return set_error(VGGT_ATTN_EINVAL, "model must be VGGT_ATTN_MODEL_VGGT or VGGT_ATTN_MODEL_PI3");
+  if (layer < 0 || layer >= kGlobalLayers)
+    return set_error(VGGT_ATTN_EINVAL, "layer " + std::to_string(layer) + " not in [0, 24)");
+  if (sigma != 1 && sigma != 2 && sigma != 4 && sigma != 6 && sigma != 9)
+    return set_error(VGGT_ATTN_EINVAL, "sigma " + std::to_string(sigma) + " not in {1, 2, 4, 6, 9}");
+  int s = 1;
+  unsigned f = 0;
+  if (layer < t_early) {
+    f = VGGT_ATTN_G2F;
+  } else if (layer < kLateFrom) {
+    s = sigma;
+    if (sigma > 1) f = VGGT_ATTN_DIAG | VGGT_ATTN_MEAN | (model == VGGT_ATTN_MODEL_VGGT ? VGGT_ATTN_REF_DENSE : 0u);
+  }
+  if (out_sigma) *out_sigma = s;
+  if (out_flags) *out_flags = f;
+  return ok();
+}
+
 int vggt_attn_copy_index_set(const vggt_attn_plan_t* plan, const void* workspace,
                              int32_t* host_idx, int32_t* host_dcount, void* stream) {
   if (!plan || !workspace) return set_error(VGGT_ATTN_EINVAL, "NULL argument");
