@@ -29,6 +29,9 @@ sys.path.insert(0, ROOT)
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak (vendor figure)
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
+# float32 vector FMA rate without packed (two-wide) instructions, which this library does not use:
+# 256 CUs x 4 SIMDs x 16 lanes x 2 flop x 2.4 GHz (the published 157.3 TFLOP/s counts packed FP32)
+FP32_VECTOR_PEAK_TFLOPS = 78.6
 
 METRIC = "global-attn attended queries/s + TFLOP/s (% bf16 MFMA peak), 800 frames sigma=6"
 
@@ -76,6 +79,9 @@ SWEEP_200 = [dict(_D200, sigma=1)] + [
     dict(_D200, g2f=True)]
 EXTRA_GROUPS = [
     ("tiny-fp32", [dict(frames=4, grid_h=8, grid_w=8, heads=2, sigma=4, diag=True, mean=True)], "fp32"),
+    # The float32 path (one lane per query on the VALU, no matrix cores) at a mid-size geometry, so
+    # that its cost beyond the tiny workload is on record.
+    ("sga4-32f-fp32", [dict(frames=32, grid_h=37, grid_w=37, heads=16, sigma=4, diag=True, mean=True)], "fp32"),
     ("dense+g2m-32f", [WORKLOADS["dense-32f"][0], WORKLOADS["dense-32f-f16"][0], WORKLOADS["g2m-32f"][0]], "bf16"),
     ("sga4-100f", [WORKLOADS["sga4-100f"][0]], "bf16"),
     ("g2f+sga9-200f", [WORKLOADS["g2f-200f"][0], WORKLOADS["sga9-200f"][0]], "bf16"),
@@ -232,9 +238,12 @@ def time_calls(plans, tensors, outs, wss, steps, warmup):
 def attention_entry(d, secs, flops, plan) -> dict:
     """One form's attention-stage time against its roofline: the bf16 MFMA peak, or for G2M (a
     broadcast of the mean value: out = v-bar, nothing to multiply) HBM bandwidth on its output
-    writes."""
+    writes, or for float32 plans the float32 vector ALU rate."""
     e = {"form": form_name(d), "ms": secs * 1e3, "kv_tokens": plan.counts()["n_kv"],
          "tflops": flops / secs / 1e12, "frac_bf16_peak": flops / secs / 1e12 / MFMA_BF16_PEAK_TFLOPS}
+    if plan.in_dtype == "fp32":
+        e.update({"bound": "alu", "peak_fp32_tflops": FP32_VECTOR_PEAK_TFLOPS,
+                  "frac_fp32_peak": flops / secs / 1e12 / FP32_VECTOR_PEAK_TFLOPS})
     if d.get("g2m"):
         out_bytes = plan.T * d["heads"] * 64 * 4
         e.update({"bound": "hbm", "out_bytes": out_bytes, "GB/s": out_bytes / secs / 1e9,
