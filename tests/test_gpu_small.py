@@ -45,6 +45,13 @@ CASES = [
     (Desc(5, 6, 1, 2, sigma=2, diag=True, mean=True, mean_count=True, phase_shift=True, ref_dense=False),
      "sga2-phase-empty-sets"),
     (Desc(4, 13, 11, 2, g2m=True), "g2m"),
+    # G2F frame lengths around the first-half-only last key tile (<= 32 keys in range) and the
+    # query blocks a wave runs in a frame's short last item: L = 70 (two tiles, 6 keys in the
+    # last), 96 (32: the boundary), 97 (33: the whole tile), 203 (four tiles, 11 keys)
+    (Desc(5, 5, 13, 3, g2f=True), "g2f-L70"),
+    (Desc(4, 7, 13, 2, g2f=True), "g2f-L96"),
+    (Desc(4, 2, 46, 2, g2f=True), "g2f-L97"),
+    (Desc(3, 9, 22, 2, g2f=True), "g2f-L203"),
 ]
 NEW = {c[1]: c for c in CASES[11:]}
 
