@@ -17,10 +17,13 @@ bfloat16 with round-to-nearest-even (or kept as float32 for fp32 workloads).  Th
 makes the same grid position correlate across frames, the structure that global attention in
 VGGT matches across views.
 
-Random streams: PCG64 seeded by numpy SeedSequence(entropy=seed, spawn_key=...), one stream for
-u of each tensor (spawn_key=(tensor, 0)) and one per frame for its noise
-(spawn_key=(tensor, 1, frame)), tensor 0/1/2 = Q/K/V.  Frames are independent streams so that
-the 800-frame workload can be drawn on all host cores in a few seconds.
+Random stream: one numpy Generator(PCG64(seed)), drawn in this order: for X in (Q, K, V), first
+u_X as one (H, L, d) float32 standard-normal array, then the noise of frame 0, 1, ..., N-1, each
+one (H, L, d) float32 array.  The draws are sequential; combining and rounding run on all host
+cores beside them.  `per_frame_streams=True` swaps in independent streams instead (PCG64 from
+SeedSequence(entropy=seed, spawn_key=(tensor, 0)) for u and (tensor, 1, frame) for each frame's
+noise, tensor 0/1/2 = Q/K/V), which draw in parallel: used only for the largest edge-case
+geometry, whose billions of values one stream draws too slowly.
 """
 from __future__ import annotations
 
@@ -73,34 +76,57 @@ def _rng(seed: int, *key: int) -> np.random.Generator:
 
 def make_qkv(frames: int, grid_h: int, grid_w: int, n_special: int, heads: int, head_dim: int,
              dtype: str = "bf16", seed: int = 0, workers: int | None = None,
-             shared: float = 0.7, noise: float = 0.7, tie_qk: bool = False):
+             shared: float = 0.7, noise: float = 0.7, tie_qk: bool = False,
+             per_frame_streams: bool = False):
     """Draw Q, K, V of shape [heads][frames*L][head_dim].
 
     dtype "bf16" returns uint16 arrays of bfloat16 bits; "fp32" returns float32 arrays.
-    The same (geometry, seed) always gives the same bytes, whatever the worker count.
-    tie_qk: K takes Q's per-position component (a stress input: a query's logits then peak at
-    its own slot in every frame)."""
+    The same (geometry, seed, per_frame_streams) always gives the same bytes, whatever the
+    worker count.  tie_qk: K takes Q's per-position component u_Q (a stress input: a query's
+    logits then peak at its own slot in every frame); u_K is still drawn, so the noise draws
+    keep their places in the stream."""
     if dtype not in ("bf16", "fp32"):
         raise ValueError(f"dtype must be 'bf16' or 'fp32', got {dtype!r}")
     L = tokens_per_frame(grid_h, grid_w, n_special)
     T = frames * L
     out_dtype = np.uint16 if dtype == "bf16" else np.float32
     workers = workers or host_threads()
+    shape = (heads, L, head_dim)
+    rng = np.random.Generator(np.random.PCG64(seed))
     result = {}
+    u_q = None
     with ThreadPoolExecutor(max_workers=workers) as pool:
         for ti, name in enumerate(("q", "k", "v")):
-            u = _rng(seed, 0 if (tie_qk and name == "k") else ti, 0).standard_normal(
-                (heads, L, head_dim), dtype=np.float32)
+            if per_frame_streams:
+                u = _rng(seed, 0 if (tie_qk and name == "k") else ti, 0).standard_normal(shape, dtype=np.float32)
+            else:
+                u = rng.standard_normal(shape, dtype=np.float32)
+                if name == "q":
+                    u_q = u.copy()
+                elif tie_qk and name == "k":
+                    u = u_q.copy()
             u *= np.float32(shared)
             x = np.empty((heads, T, head_dim), dtype=out_dtype)
 
-            def fill(f: int, ti=ti, u=u, x=x):
-                nz = _rng(seed, ti, 1, f).standard_normal((heads, L, head_dim), dtype=np.float32)
+            def finish(f: int, nz: np.ndarray, u=u, x=x):
                 nz *= np.float32(noise)
                 nz += u
                 x[:, f * L:(f + 1) * L, :] = f32_to_bf16_bits(nz) if dtype == "bf16" else nz
 
-            list(pool.map(fill, range(frames)))
+            if per_frame_streams:
+                def fill(f: int, ti=ti):
+                    finish(f, _rng(seed, ti, 1, f).standard_normal(shape, dtype=np.float32))
+
+                list(pool.map(fill, range(frames)))
+            else:
+                # the draws stay in stream order; at most 2 * workers frames wait to be finished
+                pending = []
+                for f in range(frames):
+                    pending.append(pool.submit(finish, f, rng.standard_normal(shape, dtype=np.float32)))
+                    if len(pending) >= 2 * workers:
+                        pending.pop(0).result()
+                for fut in pending:
+                    fut.result()
             result[name] = x
     return result["q"], result["k"], result["v"]
 

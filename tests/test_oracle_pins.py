@@ -490,6 +490,30 @@ def test_generator_reproducible_and_worker_independent():
         assert x.dtype == np.uint16 and np.array_equal(x, y)
     c = make_qkv(3, 4, 5, 5, 2, 64, "bf16", seed=4)
     assert not np.array_equal(a[0], c[0])
+    p1 = make_qkv(3, 4, 5, 5, 2, 64, "bf16", seed=3, workers=1, per_frame_streams=True)
+    p4 = make_qkv(3, 4, 5, 5, 2, 64, "bf16", seed=3, workers=4, per_frame_streams=True)
+    for x, y in zip(p1, p4):
+        assert np.array_equal(x, y)
+
+
+def test_generator_single_stream_order():
+    """One PCG64(seed) stream: u_Q, Q's per-frame noise, then u_K, K's noise, then V's; each value
+    0.7 u + 0.7 noise in float32, rounded to bf16; tie_qk gives K the same u as Q."""
+    frames, gh, gw, ns, H, d = 3, 4, 5, 5, 2, 64
+    L = ns + gh * gw
+    got = make_qkv(frames, gh, gw, ns, H, d, "bf16", seed=3)
+    tied = make_qkv(frames, gh, gw, ns, H, d, "bf16", seed=3, tie_qk=True)
+    rng = np.random.Generator(np.random.PCG64(3))
+    us = []
+    for x, xt in zip(got, tied):
+        u = rng.standard_normal((H, L, d), np.float32)
+        us.append(u)
+        for f in range(frames):
+            nz = rng.standard_normal((H, L, d), np.float32)
+            assert np.array_equal(x[:, f * L:(f + 1) * L], f32_to_bf16_bits(np.float32(0.7) * u + np.float32(0.7) * nz))
+            ut = us[0] if len(us) == 2 else u
+            assert np.array_equal(xt[:, f * L:(f + 1) * L],
+                                  f32_to_bf16_bits(np.float32(0.7) * ut + np.float32(0.7) * nz))
 
 
 def test_generator_shared_position_structure():
