@@ -200,14 +200,7 @@ void attn_bf16_kernel(AttnArgs a) {
   const ItemRows ir = item_rows(a, item, BM);
   const int h = ir.h;
   const int64_t row0 = ir.row0, row_end = ir.row_end, seg = ir.seg;
-  // Query block qb of this wave holds rows qrow0 + qb * kQStride .. +15.  The global forms give
-  // each wave WQ consecutive rows; G2F interleaves the waves block by block (wave w takes rows
-  // qb * 64 + w * 16 of the item), so that the rows of the last, short item of a frame fall to
-  // as few query blocks per wave as possible, and a wave runs only its `na` blocks with a row in
-  // range (a prefix, since rows grow with qb).
-  constexpr int kQStride = INPLACE ? 64 : 16;
-  const int64_t qrow0 = row0 + int64_t(wave) * (INPLACE ? 16 : WQ);
-  const int na = int(min(int64_t(QB), max(int64_t(0), (row_end - qrow0 + kQStride - 1) / kQStride)));
+  const int64_t wrow0 = row0 + int64_t(wave) * WQ;
 
   const uint16_t* Q = static_cast<const uint16_t*>(a.q) + size_t(h) * size_t(a.T) * kHeadDim;
   const uint16_t* Kin = static_cast<const uint16_t*>(a.k) + size_t(h) * size_t(a.T) * kHeadDim;
@@ -282,7 +275,7 @@ void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
     for (int cc = 0; cc < 2; ++cc)
       qraw[qb][cc] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-          qrsrc, int(qrow0 + qb * kQStride + l16) * 128 + cc * 64 + grp * 16, 0, 0));
+          qrsrc, int(wrow0 + qb * 16 + l16) * 128 + cc * 64 + grp * 16, 0, 0));
 
   // Global -> LDS copy of one 64x128-byte tile with buffer_load_dwordx4 ... lds: lane L of a wave
   // instruction writes the 16 bytes at LDS base + 16*L, so each lane fetches the global chunk
@@ -362,22 +355,26 @@ void attn_bf16_kernel(AttnArgs a) {
       }
     }
   };
+  // Compile-time counts for the helpers below: 16-key groups scored (4, or 2 for a last tile
+  // whose keys in range all lie in its first half) and 32-key halves weighted and accumulated
+  // (2, or 1).  Tags rather than int arguments, so that the full-tile code is instantiated
+  // exactly as it is written, with no folded guards.
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I4 = std::integral_constant<int, 4>;
   // S^T = K Q^T for 64 keys x the 16 queries of block qb: s[k4][i] is key k4*16 + grp*4 + i.
   // Exact mode starts each two-MFMA chain from a zero accumulator (an inline constant, so the
   // first MFMA reads no accumulator registers and the second takes its input straight from the
   // first); the running max is applied in the exp argument.  The f16 score form starts it from
   // `from` = -(m + w), so the scores leave the matrix core already shifted.
   // Size-aware keys start the chain from the keys' biases instead (read from LDS).
-  // Only the first nk4 16-key groups are formed (nk4 < 4 for a last tile whose keys in range
+  // Only the first NK4 16-key groups are formed (NK4 = 2 for a last tile whose keys in range
   // all lie in its first half); the others are set to -inf, weight 0.
   auto scores_qb = [&](const bf16x8_t (&kf)[4][2], const float* bb, int qb, f32x4_t (&s)[4], float from,
-                       int nk4 = 4) {
+                       auto nk4_tag) {
+    constexpr int NK4 = decltype(nk4_tag)::value;
 #pragma unroll
-    for (int k4 = 0; k4 < 4; ++k4) {
-      if (k4 >= nk4) {
-        s[k4] = f32x4_t{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-        continue;
-      }
+    for (int k4 = 0; k4 < NK4; ++k4) {
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
       if constexpr (PRESCALE_Q) {
         acc = f32x4_t{from, from, from, from};
@@ -391,10 +388,11 @@ void attn_bf16_kernel(AttnArgs a) {
         s[k4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[k4][1], qf[qb][1], acc, 0, 0, 0);
       }
     }
+#pragma unroll
+    for (int k4 = NK4; k4 < 4; ++k4) s[k4] = f32x4_t{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
   };
   // Mean-key bias and padding mask, only for the last tiles of the segment.
-  auto bias_mask = [&](int j, auto& s) {
-    constexpr int NQ = std::extent_v<std::remove_reference_t<decltype(s)>>;
+  auto bias_mask = [&](int j, f32x4_t (&s)[QB][4]) {
     if (j < slow_from) return;
 #pragma unroll
     for (int k4 = 0; k4 < 4; ++k4) {
@@ -408,7 +406,7 @@ void attn_bf16_kernel(AttnArgs a) {
         }
         const float add = key >= nkeys ? -INFINITY : bias;
 #pragma unroll
-        for (int qb = 0; qb < NQ; ++qb) s[qb][k4][i] += add;
+        for (int qb = 0; qb < QB; ++qb) s[qb][k4][i] += add;
       }
     }
   };
@@ -427,15 +425,15 @@ void attn_bf16_kernel(AttnArgs a) {
   // same rounded weights).
   // Returns the OR of the packed bf16 words: every p >= 0, so some p >= 2 (a score more than
   // w + 1 octaves above the running max) exactly when bit 14 of some half is set.
-  // nh = 1: only the first 32 keys (pf[0]); the caller then uses pf[0] alone.
-  auto probs_qb = [&](int qb, const f32x4_t (&s)[4], bf16x8_t (&pf)[2], int nh = 2) {
+  // NH = 1: only the first 32 keys (pf[0]), and the caller uses pf[0] alone.
+  auto probs_qb = [&](int qb, const f32x4_t (&s)[4], bf16x8_t (&pf)[2], auto nh_tag) {
+    constexpr int NH = decltype(nh_tag)::value;
     const float off = m_run[qb];
     auto e = [&](float x) { return (__bf16)__builtin_amdgcn_exp2f(PRESCALE_Q ? x : fmaf(x, c, off)); };
     uint32_t bits = 0;
     float l = l_run[qb];
 #pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) {
-      if (h2 >= nh) continue;
+    for (int h2 = 0; h2 < NH; ++h2) {
       const f32x4_t& s0 = s[2 * h2];
       const f32x4_t& s1 = s[2 * h2 + 1];
       const bf16x8_t pv = {e(s0[0]), e(s0[1]), e(s0[2]), e(s0[3]), e(s1[0]), e(s1[1]), e(s1[2]), e(s1[3])};
@@ -452,15 +450,16 @@ void attn_bf16_kernel(AttnArgs a) {
     if constexpr (!kMfmaSum) l_run[qb] = l;
     return bits;
   };
-  auto accumulate_qb = [&](const bf16x8_t (&vf)[4][2], int qb, const bf16x8_t (&pf)[2], int nh = 2) {
+  auto accumulate_qb = [&](const bf16x8_t (&vf)[4][2], int qb, const bf16x8_t (&pf)[2], auto nh_tag) {
+    constexpr int NH = decltype(nh_tag)::value;
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
       o[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[db][0], pf[0], o[qb][db], 0, 0, 0);
-      if (nh > 1) o[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[db][1], pf[1], o[qb][db], 0, 0, 0);
+      if constexpr (NH > 1) o[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[db][1], pf[1], o[qb][db], 0, 0, 0);
     }
     if constexpr (kMfmaSum) {
       l_acc[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones8, pf[0], l_acc[qb], 0, 0, 0);
-      if (nh > 1) l_acc[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones8, pf[1], l_acc[qb], 0, 0, 0);
+      if constexpr (NH > 1) l_acc[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones8, pf[1], l_acc[qb], 0, 0, 0);
     }
   };
   // Softmax of query block qb of the tile in hand, with the block's next-tile scores formed on
@@ -468,10 +467,10 @@ void attn_bf16_kernel(AttnArgs a) {
   // the current m; only if some weight reaches 2 is m raised exactly to the row max (O and l
   // rescaled) and the block redone, so in the steady state no per-score max and no rescale run.
   auto block = [&](const bf16x8_t (&kf)[4][2], const float* bb, int qb, f32x4_t (&s_cur)[4],
-                   f32x4_t (&s_next)[4], bf16x8_t (&pf)[2], bool next, int nk4_next = 4, int nh = 2) {
-    if (next) scores_qb(kf, bb, qb, s_next, m_run[qb], nk4_next);
+                   f32x4_t (&s_next)[4], bf16x8_t (&pf)[2], bool next, auto nk4_tag, auto nh_tag) {
+    if (next) scores_qb(kf, bb, qb, s_next, m_run[qb], nk4_tag);
     const float l_prev = l_run[qb];
-    const uint32_t bits = probs_qb(qb, s_cur, pf, nh);
+    const uint32_t bits = probs_qb(qb, s_cur, pf, nh_tag);
     // (expected false: the rescale is laid out of line, so the common path runs straight on)
     if (__builtin_expect(__builtin_amdgcn_ballot_w64((bits & 0x40004000u) != 0) != 0, 0)) {
       asm volatile("; rare rescale" ::);  // keeps this branch from being speculated into every tile
@@ -492,7 +491,7 @@ void attn_bf16_kernel(AttnArgs a) {
           if (next) s_next[k] -= d;
         }
       }
-      probs_qb(qb, s_cur, pf, nh);
+      probs_qb(qb, s_cur, pf, nh_tag);
     }
   };
 
@@ -506,7 +505,7 @@ void attn_bf16_kernel(AttnArgs a) {
   // Q in the B-operand layout, and the diagonal term's initial state.
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    const int64_t t = qrow0 + qb * kQStride + l16;
+    const int64_t t = wrow0 + qb * 16 + l16;
     const bool valid = t < row_end;
     float dot = 0.f;
     // The diagonal term belongs to one piece of a split item only.
@@ -579,7 +578,7 @@ void attn_bf16_kernel(AttnArgs a) {
   // computes nothing: it only copies its share of every tile and meets every barrier of the
   // steps below (one after tile 0, one per step), leaving its SIMD to the other work-group's
   // wave.  (Wave 0 always has rows, so the bias copies of wave 0 never take this path.)
-  if (na == 0) {
+  if (wrow0 >= row_end) {
     wait_tiles();
     __syncthreads();
     for (int jj = 0; jj + 1 < nkt; ++jj) {
@@ -593,17 +592,13 @@ void attn_bf16_kernel(AttnArgs a) {
     return;
   }
 
-  // Everything from here on runs the wave's NA active query blocks (NA = QB but in the short
-  // last item of a G2F frame).
-  auto run = [&](auto na_tag) {
-  constexpr int NA = decltype(na_tag)::value;
   // One pipelined step: finish tile j (scores s_cur) while the scores of tile j+1 are formed,
   // query block by query block so that every stretch of code mixes matrix-core and VALU work.
   // P = j & 1 is a compile-time constant, so every LDS buffer is static.  MASK = tile j+1 may
   // hold mean keys or padding (kept out of the steady-state loop, where the compiler would
   // otherwise if-convert the bias into every tile).
-  auto step = [&](auto parity, auto mask_tag, int j, f32x4_t (&s_cur)[NA][4], f32x4_t (&s_next)[NA][4],
-                  int nk4_next = 4) {
+  auto step = [&](auto parity, auto mask_tag, int j, f32x4_t (&s_cur)[QB][4], f32x4_t (&s_next)[QB][4],
+                  auto nk4_tag) {
     constexpr int P = decltype(parity)::value;
     using same_t = std::integral_constant<int, P>;
     using other_t = std::integral_constant<int, P ^ 1>;
@@ -614,23 +609,23 @@ void attn_bf16_kernel(AttnArgs a) {
     k_frags(kbuf(other_t{}), kf);
     v_frags(vbuf(same_t{}), vf);
 #pragma unroll
-    for (int qb = 0; qb < NA; ++qb) {
+    for (int qb = 0; qb < QB; ++qb) {
       bf16x8_t pf[2];
-      block(kf, bbuf(other_t{}), qb, s_cur[qb], s_next[qb], pf, true, nk4_next);
-      accumulate_qb(vf, qb, pf);
+      block(kf, bbuf(other_t{}), qb, s_cur[qb], s_next[qb], pf, true, nk4_tag, I2{});
+      accumulate_qb(vf, qb, pf, I2{});
     }
     if constexpr (decltype(mask_tag)::value) bias_mask(j + 1, s_next);
     wait_tiles();
     __syncthreads();
   };
-  auto last = [&](auto parity, f32x4_t (&s_cur)[NA][4], int nh = 2) {
+  auto last = [&](auto parity, f32x4_t (&s_cur)[QB][4], auto nh_tag) {
     bf16x8_t kf[4][2], vf[4][2];
     v_frags(vbuf(parity), vf);
 #pragma unroll
-    for (int qb = 0; qb < NA; ++qb) {
+    for (int qb = 0; qb < QB; ++qb) {
       bf16x8_t pf[2];
-      block(kf, nullptr, qb, s_cur[qb], s_cur[qb], pf, false, 4, nh);
-      accumulate_qb(vf, qb, pf, nh);
+      block(kf, nullptr, qb, s_cur[qb], s_cur[qb], pf, false, I4{}, nh_tag);
+      accumulate_qb(vf, qb, pf, nh_tag);
     }
   };
   using plain_t = std::integral_constant<bool, false>;
@@ -639,16 +634,16 @@ void attn_bf16_kernel(AttnArgs a) {
   using odd_t = std::integral_constant<int, 1>;
 
   // Tile 0 sets the running max exactly (from the diagonal term, if any, and the tile).
-  f32x4_t sa[NA][4], sb[NA][4];
+  f32x4_t sa[QB][4], sb[QB][4];
   {
     bf16x8_t kf[4][2];
     k_frags(kbuf0, kf);
 #pragma unroll
-    for (int qb = 0; qb < NA; ++qb) scores_qb(kf, bbuf0, qb, sa[qb], 0.f);
+    for (int qb = 0; qb < QB; ++qb) scores_qb(kf, bbuf0, qb, sa[qb], 0.f, I4{});
   }
   bias_mask(0, sa);
 #pragma unroll
-  for (int qb = 0; qb < NA; ++qb) {
+  for (int qb = 0; qb < QB; ++qb) {
     const float m_new = vmax(m_run[qb], row_max(sa[qb]));  // finite: tile 0 holds a valid key
     if constexpr (!INPLACE) {  // (without a diagonal term l and O are still zero)
       const float alpha = __builtin_amdgcn_exp2f((m_run[qb] - m_new) * sc);
@@ -668,30 +663,36 @@ void attn_bf16_kernel(AttnArgs a) {
   __syncthreads();
   int j = 0;  // always even at the top of these loops
   for (; j + 2 < nkt && j + 2 < slow_from; j += 2) {
-    step(even_t{}, plain_t{}, j, sa, sb);
-    step(odd_t{}, plain_t{}, j + 1, sb, sa);
+    step(even_t{}, plain_t{}, j, sa, sb, I4{});
+    step(odd_t{}, plain_t{}, j + 1, sb, sa, I4{});
   }
   for (; j + 2 < nkt; j += 2) {
-    step(even_t{}, masked_t{}, j, sa, sb);
-    step(odd_t{}, masked_t{}, j + 1, sb, sa);
+    step(even_t{}, masked_t{}, j, sa, sb, I4{});
+    step(odd_t{}, masked_t{}, j + 1, sb, sa, I4{});
   }
   if (j + 1 < nkt) {
     // G2F: when every key in range of the last tile lies in its first half (30 keys of a
     // 1374-token frame), that tile is scored, weighted and accumulated on the first half only.
-    const bool half = INPLACE && nkeys - (nkt - 1) * kTile <= kTile / 2;
-    step(even_t{}, masked_t{}, j, sa, sb, half ? 2 : 4);
-    last(odd_t{}, sb, half ? 1 : 2);
+    if (INPLACE && nkeys - (nkt - 1) * kTile <= kTile / 2) {
+      if constexpr (INPLACE) {
+        step(even_t{}, masked_t{}, j, sa, sb, I2{});
+        last(odd_t{}, sb, I1{});
+      }
+    } else {
+      step(even_t{}, masked_t{}, j, sa, sb, I4{});
+      last(odd_t{}, sb, I2{});
+    }
   } else {
-    last(even_t{}, sa);
+    last(even_t{}, sa, I2{});
   }
 
   // ---- epilogue: O / l, or the unnormalised state of a piece ----
   if constexpr (SPLIT) {
     float* dst = a.part + size_t(blockIdx.x) * BM * kPartRow;
 #pragma unroll
-    for (int qb = 0; qb < NA; ++qb) {
+    for (int qb = 0; qb < QB; ++qb) {
       const float l = kMfmaSum ? l_acc[qb][0] : group_sum(l_run[qb]);
-      float* row = dst + size_t((qrow0 - row0) + qb * kQStride + l16) * kPartRow;
+      float* row = dst + size_t(wave * WQ + qb * 16 + l16) * kPartRow;
 #pragma unroll
       for (int db = 0; db < 4; ++db) *reinterpret_cast<f32x4_t*>(row + db * 16 + grp * 4) = o[qb][db];
       if (grp == 0) {
@@ -702,10 +703,10 @@ void attn_bf16_kernel(AttnArgs a) {
     return;
   }
 #pragma unroll
-  for (int qb = 0; qb < NA; ++qb) {
+  for (int qb = 0; qb < QB; ++qb) {
     const float l = kMfmaSum ? l_acc[qb][0] : group_sum(l_run[qb]);
     const float inv = __builtin_amdgcn_rcpf(l);
-    const int64_t t = qrow0 + qb * kQStride + l16;
+    const int64_t t = wrow0 + qb * 16 + l16;
     if (t >= row_end) continue;
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
@@ -718,15 +719,6 @@ void attn_bf16_kernel(AttnArgs a) {
         *reinterpret_cast<f32x4_t*>(static_cast<float*>(a.out) + off) = r;
       }
     }
-  }
-  };
-  if constexpr (INPLACE) {
-    static_assert(QB <= 3, "G2F runs 1..3 query blocks per wave");
-    if (na >= QB) run(std::integral_constant<int, QB>{});
-    else if (QB == 3 && na == 2) run(std::integral_constant<int, (QB == 3 ? 2 : 1)>{});
-    else run(std::integral_constant<int, 1>{});
-  } else {
-    run(std::integral_constant<int, QB>{});
   }
 }
 
