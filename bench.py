@@ -294,22 +294,18 @@ def timed_group(dev, name, descs, dtype, tensors, steps):
     return entry
 
 
-def scheduled_pass(dev, frames: int, sigma: int, steps: int, model: str = "vggt") -> dict:
+def scheduled_pass(dev, frames: int, sigma: int, steps: int, qkv, model: str = "vggt") -> dict:
     """One pass over the 24 global layers of `model` under AVGGT's schedule ("AVGGT" notes,
-    整体框架: G2F below t_early, enhanced SGA sigma in the middle, dense for layers 20-23), each
-    layer a full forward (pack + attend) on shared synthetic Q/K/V; beside it, 24 times the
-    measured time of a dense layer, the cost of the same 24 layers without the schedule."""
-    import numpy as np
+    整体框架: G2F below t_early -- 9 for VGGT, 10 for pi^3 --, enhanced SGA sigma in the middle,
+    dense for layers 20-23), each layer a full forward (pack + attend) on the given device Q/K/V
+    of `frames` frames; beside it, 24 times the measured time of a dense layer, the cost of the
+    same 24 layers without the schedule."""
     import torch
 
     import vggt_global_attention_attn_amd as va
-    from synth import make_qkv
 
     sl = va.ScheduledLayers(frames, 37, 37, 16, model=model, sigma=sigma, device=dev)
-    q, k, v = make_qkv(frames, 37, 37, 5, 16, 64, "bf16", seed=0)
-    up = lambda x: torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
-    qd, kd, vd = up(q), up(k), up(v)
-    del q, k, v
+    qd, kd, vd = qkv
     outs = [p.new_output(dev) for p in sl.plans]
     for layer in range(va.GLOBAL_LAYERS):  # warm-up pass (also allocates the workspaces)
         sl.forward(layer, qd, kd, vd, outs[sl.index[layer]])
@@ -332,7 +328,7 @@ def scheduled_pass(dev, frames: int, sigma: int, steps: int, model: str = "vggt"
         by_form.setdefault(name, []).append(per_layer[layer])
     forms = {n: {"layers": len(t), "ms_per_layer": sum(t) / len(t)} for n, t in by_form.items()}
     dense_ms = forms["dense"]["ms_per_layer"]
-    entry = {"name": f"avggt{sigma}-24layers-{frames}f", "model": model, "sigma": sigma, "frames": frames,
+    entry = {"name": f"avggt{sigma}-24layers-{frames}f" + ("" if model == "vggt" else f"-{model}"), "model": model, "sigma": sigma, "frames": frames,
              "ms_per_pass": wall * 1e3, "sum_of_layer_ms": sum(per_layer), "tflops": sl.flops() / wall / 1e12,
              "forms": forms, "dense_24_layers_ms": 24 * dense_ms,
              "speedup_vs_24_dense_layers": 24 * dense_ms / (wall * 1e3)}
@@ -368,7 +364,14 @@ def extra_workloads(dev, steps: int):
         results.append(timed_group(dev, name, descs, dtype, shared[key], steps))
     shared.clear()
     torch.cuda.empty_cache()
-    results.append(scheduled_pass(dev, 100, 9, steps=2))
+    q, k, v = make_qkv(100, 37, 37, 5, 16, 64, "bf16", seed=0)
+    up = lambda x: torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(dev)
+    qkv = (up(q), up(k), up(v))
+    del q, k, v
+    for model in ("vggt", "pi3"):
+        results.append(scheduled_pass(dev, 100, 9, steps=2, qkv=qkv, model=model))
+    del qkv
+    torch.cuda.empty_cache()
     return results
 
 

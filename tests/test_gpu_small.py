@@ -593,16 +593,18 @@ def test_random_configs_fp32(lib, case):
     assert_close(out.cpu().numpy(), ref, fp32=True, label=f"random-fp32-{case}")
 
 
-def test_scheduled_layers_match_oracle(lib):
-    """The 24 global layers of VGGT under AVGGT's schedule (sigma 4) on one set of inputs, run by
-    the scheduled driver: each layer's output equals the oracle's for that layer's form (G2F for
-    0-8, enhanced SGA for 9-19, dense for 20-23), and layers of one form give identical bits."""
+@pytest.mark.parametrize("model", ["vggt", "pi3"])
+def test_scheduled_layers_match_oracle(lib, model):
+    """The 24 global layers of VGGT (pi^3) under AVGGT's schedule (sigma 4) on one set of inputs,
+    run by the scheduled driver: each layer's output equals the oracle's for that layer's form
+    (G2F for 0-8 (0-9), enhanced SGA for 9-19 (10-19) with frame 0 dense for VGGT only, dense for
+    20-23), and layers of one form give identical bits."""
     import torch
     import vggt_global_attention_attn_amd as va
     d0 = Desc(6, 13, 11, 2, sigma=4, diag=True, mean=True)
     q, k, v = inputs_for(d0, "bf16", seed=41)
     qd, kd, vd = to_device(q), to_device(k), to_device(v)
-    sl = va.ScheduledLayers(6, 13, 11, 2, model="vggt", sigma=4)
+    sl = va.ScheduledLayers(6, 13, 11, 2, model=model, sigma=4)
     outs = []
     for layer in range(24):
         out = sl.plan(layer).new_output().fill_(float("nan"))
@@ -610,7 +612,7 @@ def test_scheduled_layers_match_oracle(lib):
         outs.append(out)
     torch.cuda.synchronize()
     refs = {}
-    for layer, kw in enumerate(va.layer_schedule("vggt", 4)):
+    for layer, kw in enumerate(va.layer_schedule(model, 4)):
         desc = Desc(6, 13, 11, 2, sigma=kw["sigma"], g2f=kw["g2f"], ref_dense=kw["ref_dense"], diag=kw["diag"],
                     mean=kw["mean"])
         key = (kw["sigma"], kw["g2f"], kw["diag"])
