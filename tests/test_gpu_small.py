@@ -623,3 +623,57 @@ def test_scheduled_layers_match_oracle(lib, model):
         assert_close(got, ref, fp32=False, label=f"layer {layer}")
         assert torch.equal(outs[layer], first)
     assert len(refs) == 3
+
+
+# Guard-padded buffers: the output and the workspace sit inside larger allocations whose
+# 4 KiB borders hold a byte pattern, and the inputs are compared before and after; a write
+# outside [out, out + size) or [ws, ws + workspace_bytes), or into Q/K/V, changes one of them.
+# One case per kernel path: global forms with the diagonal and means (exact and f16 score
+# form, bf16 output), split pieces and their merge, G2F read in place (first-half last tile,
+# two-tile frames), G2M, size-aware keys, and the fp32 path.
+GUARDED = [
+    (Desc(3, 5, 7, 2, sigma=6, diag=True, mean=True), "sga6-enh", "bf16", "fp32", False),
+    (Desc(6, 13, 11, 2, sigma=4, diag=True, mean=True, mean_count=True), "sga4-f16", "bf16", "bf16", True),
+    (Desc(3, 37, 37, 2, sigma=1), "dense-split", "bf16", "fp32", False),
+    (Desc(4, 37, 37, 2, g2f=True), "g2f-37x37", "bf16", "bf16", False),
+    (Desc(5, 5, 13, 3, g2f=True), "g2f-L70", "bf16", "fp32", False),
+    (Desc(4, 13, 11, 2, g2m=True), "g2m", "bf16", "fp32", False),
+    (Desc(5, 13, 11, 3, sigma=4, diag=True, log_size=True), "sga4-sized", "bf16", "fp32", False),
+    (Desc(4, 8, 8, 2, sigma=4, diag=True, mean=True), "fp32-tiny", "fp32", "fp32", False),
+]
+
+
+@pytest.mark.parametrize("desc,label,in_dtype,out_dtype,prescale_q", GUARDED, ids=[c[1] for c in GUARDED])
+def test_guard_padded_buffers(lib, desc, label, in_dtype, out_dtype, prescale_q):
+    import torch
+    from synth import make_log_sizes
+    print(f"[guard] {label}", flush=True)
+    q, k, v = inputs_for(desc, in_dtype, seed=17)
+    qd, kd, vd = to_device(q), to_device(k), to_device(v)
+    before = [x.clone() for x in (qd, kd, vd)]
+    plan = lib.Plan(**plan_kwargs(desc, in_dtype, out_dtype), prescale_q=prescale_q)
+    G = 4096
+    out_dt = torch.bfloat16 if out_dtype == "bf16" else torch.float32
+    out_bytes = desc.heads * plan.T * desc.head_dim * (2 if out_dtype == "bf16" else 4)
+    ws_bytes = max(1, plan.workspace_bytes)
+    raw_out = torch.full((G + out_bytes + G,), 0xA5, dtype=torch.uint8, device="cuda")
+    raw_ws = torch.full((G + ws_bytes + G,), 0x5A, dtype=torch.uint8, device="cuda")
+    out = raw_out[G:G + out_bytes].view(out_dt).view(desc.heads, plan.T, desc.head_dim)
+    ws = raw_ws[G:G + ws_bytes]
+    lg = None
+    if desc.log_size:
+        _, lg = make_log_sizes(desc.frames, desc.grid_h, desc.grid_w, desc.n_special, seed=5)
+        plan.forward_sized(qd, kd, vd, torch.from_numpy(lg).cuda(), out, ws)
+    else:
+        plan.forward(qd, kd, vd, out, ws)
+    torch.cuda.synchronize()
+    for raw, lo, hi, pat in ((raw_out, G, G + out_bytes, 0xA5), (raw_ws, G, G + ws_bytes, 0x5A)):
+        assert bool((raw[:lo] == pat).all()) and bool((raw[hi:] == pat).all()), f"{label}: write outside a buffer"
+    for a, b in zip(before, (qd, kd, vd)):
+        assert torch.equal(a, b), f"{label}: an input changed"
+    ref = oracle.attention(q, k, v, desc, workers=4, log_g=lg)
+    got = out.float().cpu().numpy()
+    if prescale_q:  # the f16 score form on ordinary inputs: the usual bars
+        assert_close(got, ref, fp32=False, label=label)
+    else:
+        assert_close(got, ref, fp32=(in_dtype == "fp32"), label=label)
