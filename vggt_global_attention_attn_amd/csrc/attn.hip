@@ -355,26 +355,15 @@ void attn_bf16_kernel(AttnArgs a) {
       }
     }
   };
-  // Compile-time counts for the helpers below: 16-key groups scored (4, or 2 for a last tile
-  // whose keys in range all lie in its first half) and 32-key halves weighted and accumulated
-  // (2, or 1).  Tags rather than int arguments, so that the full-tile code is instantiated
-  // exactly as it is written, with no folded guards.
-  using I1 = std::integral_constant<int, 1>;
-  using I2 = std::integral_constant<int, 2>;
-  using I4 = std::integral_constant<int, 4>;
   // S^T = K Q^T for 64 keys x the 16 queries of block qb: s[k4][i] is key k4*16 + grp*4 + i.
   // Exact mode starts each two-MFMA chain from a zero accumulator (an inline constant, so the
   // first MFMA reads no accumulator registers and the second takes its input straight from the
   // first); the running max is applied in the exp argument.  The f16 score form starts it from
   // `from` = -(m + w), so the scores leave the matrix core already shifted.
   // Size-aware keys start the chain from the keys' biases instead (read from LDS).
-  // Only the first NK4 16-key groups are formed (NK4 = 2 for a last tile whose keys in range
-  // all lie in its first half); the others are set to -inf, weight 0.
-  auto scores_qb = [&](const bf16x8_t (&kf)[4][2], const float* bb, int qb, f32x4_t (&s)[4], float from,
-                       auto nk4_tag) {
-    constexpr int NK4 = decltype(nk4_tag)::value;
+  auto scores_qb = [&](const bf16x8_t (&kf)[4][2], const float* bb, int qb, f32x4_t (&s)[4], float from) {
 #pragma unroll
-    for (int k4 = 0; k4 < NK4; ++k4) {
+    for (int k4 = 0; k4 < 4; ++k4) {
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
       if constexpr (PRESCALE_Q) {
         acc = f32x4_t{from, from, from, from};
@@ -388,8 +377,6 @@ void attn_bf16_kernel(AttnArgs a) {
         s[k4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[k4][1], qf[qb][1], acc, 0, 0, 0);
       }
     }
-#pragma unroll
-    for (int k4 = NK4; k4 < 4; ++k4) s[k4] = f32x4_t{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
   };
   // Mean-key bias and padding mask, only for the last tiles of the segment.
   auto bias_mask = [&](int j, f32x4_t (&s)[QB][4]) {
@@ -425,15 +412,13 @@ void attn_bf16_kernel(AttnArgs a) {
   // same rounded weights).
   // Returns the OR of the packed bf16 words: every p >= 0, so some p >= 2 (a score more than
   // w + 1 octaves above the running max) exactly when bit 14 of some half is set.
-  // NH = 1: only the first 32 keys (pf[0]), and the caller uses pf[0] alone.
-  auto probs_qb = [&](int qb, const f32x4_t (&s)[4], bf16x8_t (&pf)[2], auto nh_tag) {
-    constexpr int NH = decltype(nh_tag)::value;
+  auto probs_qb = [&](int qb, const f32x4_t (&s)[4], bf16x8_t (&pf)[2]) {
     const float off = m_run[qb];
     auto e = [&](float x) { return (__bf16)__builtin_amdgcn_exp2f(PRESCALE_Q ? x : fmaf(x, c, off)); };
     uint32_t bits = 0;
     float l = l_run[qb];
 #pragma unroll
-    for (int h2 = 0; h2 < NH; ++h2) {
+    for (int h2 = 0; h2 < 2; ++h2) {
       const f32x4_t& s0 = s[2 * h2];
       const f32x4_t& s1 = s[2 * h2 + 1];
       const bf16x8_t pv = {e(s0[0]), e(s0[1]), e(s0[2]), e(s0[3]), e(s1[0]), e(s1[1]), e(s1[2]), e(s1[3])};
@@ -450,16 +435,15 @@ void attn_bf16_kernel(AttnArgs a) {
     if constexpr (!kMfmaSum) l_run[qb] = l;
     return bits;
   };
-  auto accumulate_qb = [&](const bf16x8_t (&vf)[4][2], int qb, const bf16x8_t (&pf)[2], auto nh_tag) {
-    constexpr int NH = decltype(nh_tag)::value;
+  auto accumulate_qb = [&](const bf16x8_t (&vf)[4][2], int qb, const bf16x8_t (&pf)[2]) {
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
       o[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[db][0], pf[0], o[qb][db], 0, 0, 0);
-      if constexpr (NH > 1) o[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[db][1], pf[1], o[qb][db], 0, 0, 0);
+      o[qb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[db][1], pf[1], o[qb][db], 0, 0, 0);
     }
     if constexpr (kMfmaSum) {
       l_acc[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones8, pf[0], l_acc[qb], 0, 0, 0);
-      if constexpr (NH > 1) l_acc[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones8, pf[1], l_acc[qb], 0, 0, 0);
+      l_acc[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones8, pf[1], l_acc[qb], 0, 0, 0);
     }
   };
   // Softmax of query block qb of the tile in hand, with the block's next-tile scores formed on
@@ -467,10 +451,10 @@ void attn_bf16_kernel(AttnArgs a) {
   // the current m; only if some weight reaches 2 is m raised exactly to the row max (O and l
   // rescaled) and the block redone, so in the steady state no per-score max and no rescale run.
   auto block = [&](const bf16x8_t (&kf)[4][2], const float* bb, int qb, f32x4_t (&s_cur)[4],
-                   f32x4_t (&s_next)[4], bf16x8_t (&pf)[2], bool next, auto nk4_tag, auto nh_tag) {
-    if (next) scores_qb(kf, bb, qb, s_next, m_run[qb], nk4_tag);
+                   f32x4_t (&s_next)[4], bf16x8_t (&pf)[2], bool next) {
+    if (next) scores_qb(kf, bb, qb, s_next, m_run[qb]);
     const float l_prev = l_run[qb];
-    const uint32_t bits = probs_qb(qb, s_cur, pf, nh_tag);
+    const uint32_t bits = probs_qb(qb, s_cur, pf);
     // (expected false: the rescale is laid out of line, so the common path runs straight on)
     if (__builtin_expect(__builtin_amdgcn_ballot_w64((bits & 0x40004000u) != 0) != 0, 0)) {
       asm volatile("; rare rescale" ::);  // keeps this branch from being speculated into every tile
@@ -491,7 +475,7 @@ void attn_bf16_kernel(AttnArgs a) {
           if (next) s_next[k] -= d;
         }
       }
-      probs_qb(qb, s_cur, pf, nh_tag);
+      probs_qb(qb, s_cur, pf);
     }
   };
 
@@ -597,8 +581,7 @@ void attn_bf16_kernel(AttnArgs a) {
   // P = j & 1 is a compile-time constant, so every LDS buffer is static.  MASK = tile j+1 may
   // hold mean keys or padding (kept out of the steady-state loop, where the compiler would
   // otherwise if-convert the bias into every tile).
-  auto step = [&](auto parity, auto mask_tag, int j, f32x4_t (&s_cur)[QB][4], f32x4_t (&s_next)[QB][4],
-                  auto nk4_tag) {
+  auto step = [&](auto parity, auto mask_tag, int j, f32x4_t (&s_cur)[QB][4], f32x4_t (&s_next)[QB][4]) {
     constexpr int P = decltype(parity)::value;
     using same_t = std::integral_constant<int, P>;
     using other_t = std::integral_constant<int, P ^ 1>;
@@ -611,21 +594,21 @@ void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       bf16x8_t pf[2];
-      block(kf, bbuf(other_t{}), qb, s_cur[qb], s_next[qb], pf, true, nk4_tag, I2{});
-      accumulate_qb(vf, qb, pf, I2{});
+      block(kf, bbuf(other_t{}), qb, s_cur[qb], s_next[qb], pf, true);
+      accumulate_qb(vf, qb, pf);
     }
     if constexpr (decltype(mask_tag)::value) bias_mask(j + 1, s_next);
     wait_tiles();
     __syncthreads();
   };
-  auto last = [&](auto parity, f32x4_t (&s_cur)[QB][4], auto nh_tag) {
+  auto last = [&](auto parity, f32x4_t (&s_cur)[QB][4]) {
     bf16x8_t kf[4][2], vf[4][2];
     v_frags(vbuf(parity), vf);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       bf16x8_t pf[2];
-      block(kf, nullptr, qb, s_cur[qb], s_cur[qb], pf, false, I4{}, nh_tag);
-      accumulate_qb(vf, qb, pf, nh_tag);
+      block(kf, nullptr, qb, s_cur[qb], s_cur[qb], pf, false);
+      accumulate_qb(vf, qb, pf);
     }
   };
   using plain_t = std::integral_constant<bool, false>;
@@ -639,7 +622,7 @@ void attn_bf16_kernel(AttnArgs a) {
     bf16x8_t kf[4][2];
     k_frags(kbuf0, kf);
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) scores_qb(kf, bbuf0, qb, sa[qb], 0.f, I4{});
+    for (int qb = 0; qb < QB; ++qb) scores_qb(kf, bbuf0, qb, sa[qb], 0.f);
   }
   bias_mask(0, sa);
 #pragma unroll
@@ -663,27 +646,18 @@ void attn_bf16_kernel(AttnArgs a) {
   __syncthreads();
   int j = 0;  // always even at the top of these loops
   for (; j + 2 < nkt && j + 2 < slow_from; j += 2) {
-    step(even_t{}, plain_t{}, j, sa, sb, I4{});
-    step(odd_t{}, plain_t{}, j + 1, sb, sa, I4{});
+    step(even_t{}, plain_t{}, j, sa, sb);
+    step(odd_t{}, plain_t{}, j + 1, sb, sa);
   }
   for (; j + 2 < nkt; j += 2) {
-    step(even_t{}, masked_t{}, j, sa, sb, I4{});
-    step(odd_t{}, masked_t{}, j + 1, sb, sa, I4{});
+    step(even_t{}, masked_t{}, j, sa, sb);
+    step(odd_t{}, masked_t{}, j + 1, sb, sa);
   }
   if (j + 1 < nkt) {
-    // G2F: when every key in range of the last tile lies in its first half (30 keys of a
-    // 1374-token frame), that tile is scored, weighted and accumulated on the first half only.
-    if (INPLACE && nkeys - (nkt - 1) * kTile <= kTile / 2) {
-      if constexpr (INPLACE) {
-        step(even_t{}, masked_t{}, j, sa, sb, I2{});
-        last(odd_t{}, sb, I1{});
-      }
-    } else {
-      step(even_t{}, masked_t{}, j, sa, sb, I4{});
-      last(odd_t{}, sb, I2{});
-    }
+    step(even_t{}, masked_t{}, j, sa, sb);
+    last(odd_t{}, sb);
   } else {
-    last(even_t{}, sa, I2{});
+    last(even_t{}, sa);
   }
 
   // ---- epilogue: O / l, or the unnormalised state of a piece ----
